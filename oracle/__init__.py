@@ -1,0 +1,208 @@
+"""CPU oracle for the fused MoE backward d_x (test infrastructure only).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product path (the
+``permute_grouped_gemm_amd`` package and its HIP library) never touches it,
+and the two share no code.
+
+The arithmetic lives in ``oracle.c`` (plain C, explicit loops, double
+accumulation), which follows the formulas of the MoeInitRoutingGroupedMatmulGrad
+design page, §数学定义和公式 (Step 1: d_expanded_x = d_y · Wᵀ per expert; Step 2:
+scatter-add of expanded rows back to their token, batch row = original
+position / topK).  ``brute.py`` evaluates the merged scalar formula of the same
+section literally, with its indicator function, for tiny inputs.
+
+Parity status: every function here is pinned by the CPU tests in
+``tests/test_oracle_*.py`` (brute force, library matmul special cases, the
+adjoint identity against an independent forward, invariants, hand-worked
+fixtures in ``tests/golden/``); nothing is "parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "oracle.c")
+LIB = os.path.join(HERE, "liboracle.so")
+
+OK, ERR_SHAPE, ERR_GROUP_NEG, ERR_GROUP_SUM, ERR_INDEX_RANGE, ERR_INDEX_DUP, ERR_ALLOC = range(7)
+SLOT, ASCEND, EXACT = 0, 1, 2
+DTYPE_CODE = {"f32": 0, "f16": 1, "bf16": 2}
+
+
+def build(force: bool = False) -> str:
+    """Compile oracle.c into liboracle.so (plain gcc, no contraction of a*b+c)."""
+    if force or not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+        tmp = LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-shared",
+                               "-fPIC", "-pthread", SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, LIB)
+    return LIB
+
+
+class _Problem(ctypes.Structure):
+    _fields_ = [("M", ctypes.c_int64), ("N", ctypes.c_int64), ("G", ctypes.c_int64),
+                ("K", ctypes.c_int64), ("batch", ctypes.c_int64), ("topk", ctypes.c_int64),
+                ("row_idx_type", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("grad_y", ctypes.c_void_p), ("weight", ctypes.c_void_p),
+                ("eri", ctypes.c_void_p), ("group_list", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        build()
+        L = ctypes.CDLL(LIB)
+        i64, i32, vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
+        PP = ctypes.POINTER(_Problem)
+        L.orc_check.argtypes = [i64] * 9 + [i32] * 3
+        L.orc_offsets.argtypes = [i64, vp, i64, vp]
+        L.orc_index.argtypes = [i64, i32, vp, vp, vp]
+        L.orc_decode.argtypes = [i32, vp, i64, vp]
+        L.orc_half_to_double.argtypes = [ctypes.c_uint16]
+        L.orc_half_to_double.restype = ctypes.c_double
+        L.orc_bf16_to_double.argtypes = [ctypes.c_uint16]
+        L.orc_bf16_to_double.restype = ctypes.c_double
+        L.orc_dex.argtypes = [PP, vp, vp, vp, ctypes.c_int]
+        L.orc_scatter.argtypes = [PP, vp, vp, vp, i32, vp, vp, vp]
+        L.orc_dx_tokens.argtypes = [PP, vp, i64, vp, vp, vp, ctypes.c_int]
+        for f in ("orc_check", "orc_offsets", "orc_index", "orc_dex", "orc_scatter", "orc_dx_tokens"):
+            getattr(L, f).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def default_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+class OracleError(RuntimeError):
+    def __init__(self, code: int, what: str = ""):
+        super().__init__(f"oracle error {code} {what}")
+        self.code = code
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data
+
+
+def _problem(grad_y, weight, eri, group_list, batch, topk, row_idx_type, dtype):
+    grad_y = np.ascontiguousarray(grad_y)
+    weight = np.ascontiguousarray(weight)
+    eri = np.ascontiguousarray(eri, dtype=np.int64)
+    group_list = np.ascontiguousarray(group_list, dtype=np.int64)
+    if grad_y.ndim != 2 or weight.ndim != 3 or eri.ndim != 1 or group_list.ndim != 1:
+        raise OracleError(ERR_SHAPE, "rank")
+    M, Ny = grad_y.shape
+    G, K, Nw = weight.shape
+    rc = lib().orc_check(M, Ny, G, K, Nw, eri.shape[0], group_list.shape[0], batch, topk,
+                         row_idx_type, DTYPE_CODE[dtype], DTYPE_CODE[dtype])
+    if rc:
+        raise OracleError(rc, "shape")
+    pr = _Problem(M, Ny, G, K, batch, topk, row_idx_type, DTYPE_CODE[dtype],
+                  grad_y.ctypes.data, weight.ctypes.data, eri.ctypes.data, group_list.ctypes.data)
+    keep = (grad_y, weight, eri, group_list)
+    return pr, keep
+
+
+def check(M, Ny, G, K, Nw, L, Gl, batch, topk, row_idx_type, dtype_y, dtype_w) -> int:
+    return lib().orc_check(M, Ny, G, K, Nw, L, Gl, batch, topk, row_idx_type,
+                           DTYPE_CODE.get(dtype_y, -1), DTYPE_CODE.get(dtype_w, -1))
+
+
+def offsets(group_list: np.ndarray, M: int) -> np.ndarray:
+    gl = np.ascontiguousarray(group_list, dtype=np.int64)
+    off = np.zeros(gl.shape[0] + 1, dtype=np.int64)
+    rc = lib().orc_offsets(gl.shape[0], gl.ctypes.data, M, off.ctypes.data)
+    if rc:
+        raise OracleError(rc, "group_list")
+    return off
+
+
+def index(eri: np.ndarray, row_idx_type: int):
+    """(ori, inv): ori[i] original position of expanded row i, inv[p] expanded row of p."""
+    eri = np.ascontiguousarray(eri, dtype=np.int64)
+    M = eri.shape[0]
+    ori = np.empty(M, dtype=np.int64)
+    inv = np.empty(M, dtype=np.int64)
+    rc = lib().orc_index(M, row_idx_type, eri.ctypes.data, ori.ctypes.data, inv.ctypes.data)
+    if rc:
+        raise OracleError(rc, "index")
+    return ori, inv
+
+
+def decode(x: np.ndarray, dtype: str) -> np.ndarray:
+    x = np.ascontiguousarray(x)
+    out = np.empty(x.size, dtype=np.float64)
+    lib().orc_decode(DTYPE_CODE[dtype], x.ctypes.data, x.size, out.ctypes.data)
+    return out.reshape(x.shape)
+
+
+def dex(grad_y, weight, eri, group_list, batch, topk, row_idx_type, dtype, *,
+        want64=False, want_abs=False, nthreads=None):
+    """Step 1: d_expanded_x rounded to float32 (and optionally the double values / |terms|)."""
+    pr, keep = _problem(grad_y, weight, eri, group_list, batch, topk, row_idx_type, dtype)
+    d32 = np.empty((pr.M, pr.K), dtype=np.float32)
+    d64 = np.empty((pr.M, pr.K), dtype=np.float64) if want64 else None
+    a64 = np.empty((pr.M, pr.K), dtype=np.float64) if want_abs else None
+    rc = lib().orc_dex(ctypes.byref(pr), _ptr(d32), _ptr(d64), _ptr(a64), nthreads or default_threads())
+    if rc:
+        raise OracleError(rc, "dex")
+    return d32, d64, a64
+
+
+def moe_dx(grad_y, weight, eri, group_list, batch, topk, row_idx_type, dtype, *,
+           mode=SLOT, want_abs=False, nthreads=None):
+    """Full d_x [batch, K].  mode SLOT / ASCEND give float32, EXACT gives float64.
+
+    With want_abs, also returns absdot[b,k] = sum over the token's terms of |d_y|·|W|."""
+    d32, d64, a64 = dex(grad_y, weight, eri, group_list, batch, topk, row_idx_type, dtype,
+                        want64=(mode == EXACT), want_abs=want_abs, nthreads=nthreads)
+    pr, keep = _problem(grad_y, weight, eri, group_list, batch, topk, row_idx_type, dtype)
+    dx32 = np.empty((batch, pr.K), dtype=np.float32) if mode != EXACT else None
+    dx64 = np.empty((batch, pr.K), dtype=np.float64) if mode == EXACT else None
+    absdot = np.empty((batch, pr.K), dtype=np.float64) if want_abs else None
+    rc = lib().orc_scatter(ctypes.byref(pr), _ptr(d32), _ptr(d64), _ptr(a64), mode,
+                           _ptr(dx32), _ptr(dx64), _ptr(absdot))
+    if rc:
+        raise OracleError(rc, "scatter")
+    out = dx64 if mode == EXACT else dx32
+    return (out, absdot) if want_abs else out
+
+
+def moe_dx_tokens(grad_y, weight, eri, group_list, batch, topk, row_idx_type, dtype, tokens, *,
+                  nthreads=None):
+    """d_x rows of the listed tokens: (slot-order float32, exact float64, absdot)."""
+    pr, keep = _problem(grad_y, weight, eri, group_list, batch, topk, row_idx_type, dtype)
+    tokens = np.ascontiguousarray(tokens, dtype=np.int64)
+    n = tokens.shape[0]
+    dx32 = np.empty((n, pr.K), dtype=np.float32)
+    dx64 = np.empty((n, pr.K), dtype=np.float64)
+    absdot = np.empty((n, pr.K), dtype=np.float64)
+    rc = lib().orc_dx_tokens(ctypes.byref(pr), tokens.ctypes.data, n, dx32.ctypes.data,
+                             dx64.ctypes.data, absdot.ctypes.data, nthreads or default_threads())
+    if rc:
+        raise OracleError(rc, "tokens")
+    return dx32, dx64, absdot
+
+
+def case_dx(case, mode=SLOT, **kw):
+    """moe_dx on a ``synth.Case``."""
+    return moe_dx(case.grad_y, case.weight, case.eri, case.group_list, case.batch, case.topk,
+                  case.row_idx_type, case.dtype, mode=mode, **kw)
+
+
+def case_dx_tokens(case, tokens, **kw):
+    return moe_dx_tokens(case.grad_y, case.weight, case.eri, case.group_list, case.batch,
+                         case.topk, case.row_idx_type, case.dtype, tokens, **kw)
