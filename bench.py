@@ -1,0 +1,230 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused MoE backward d_x on one MI355X.
+
+One step = one fused call (index preparation, grouped-GEMM producer, ordered
+scatter-add consumer) over a seeded synthetic batch whose inputs are already
+resident in HBM.  Prints one JSON line.
+
+Default workload: decode-sized bf16 (batch 16, topK 8, G 16 with 4 empty
+experts, K 7168, N 4096), where streaming the non-empty experts' weights
+dominates; `value` is its effective GB/s.  The same line carries the large
+fp16 workload (batch 13824, topK 8, G 60, K 7168, N 2048; TFLOP/s) under
+"large" unless --no-large is given.
+
+Per-kernel durations come from HIP events the library records around every
+kernel it launches (on the stream the kernels run on), inside the timed
+region.  The CPU baseline is the oracle on a bounded sample of the same
+workload, timed on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}
+METRIC = "fused d_x TFLOP/s (% bf16 MFMA peak) and GB/s (% HBM) at M=110K and M=128"
+
+
+def algorithmic(case):
+    """Algorithmic flops and bytes of one fused call (no ring / re-read traffic).
+
+    bytes = d_y + weights of non-empty experts + routing index + group_list
+    + d_x written once; flops = 2*M*N*K."""
+    import numpy as np
+    s = {"f32": 4, "f16": 2, "bf16": 2}[case.dtype]
+    g_ne = int(np.count_nonzero(case.group_list))
+    flops = 2.0 * case.M * case.N * case.K
+    bytes_ = (case.M * case.N * s + g_ne * case.K * case.N * s + 8 * case.M + 8 * case.G
+              + 4 * case.batch * case.K)
+    producer_bytes = case.M * case.N * s + g_ne * case.K * case.N * s
+    return flops, bytes_, producer_bytes
+
+
+def measure(name, steps, warmup, cpu_baseline, log):
+    import numpy as np
+    import torch
+
+    import permute_grouped_gemm_amd as pgg
+    import synth
+
+    t0 = time.time()
+    case = synth.make_config(name)
+    log(f"[bench] {name}: generated inputs in {time.time() - t0:.1f}s "
+        f"(M={case.M} N={case.N} K={case.K} G={case.G} {case.dtype})")
+    dev = torch.device("cuda:0")
+
+    def dev_tensor(a):
+        if case.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    gy, w = dev_tensor(case.grad_y), dev_tensor(case.weight)
+    eri = torch.from_numpy(case.eri).to(dev)
+    gl = torch.from_numpy(case.group_list).to(dev)
+    plan = pgg.plan(gy, w, eri, gl, case.batch, case.topk, case.row_idx_type)
+    ws = torch.empty(plan["workspace_bytes"], dtype=torch.uint8, device=dev)
+    out = torch.empty((case.batch, case.K), dtype=torch.float32, device=dev)
+
+    def step():
+        pgg.moe_dx(gy, w, eri, gl, case.batch, case.topk, case.row_idx_type, out=out, workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    code, detail = pgg.read_device_error(ws)
+    if code != 0:
+        raise RuntimeError(f"device error {code} ({detail})")
+
+    launches_per_call = 4 + 2 * plan["max_chunks"]
+    with pgg.KernelTimer(capacity=launches_per_call * steps + 16) as timer:
+        start = torch.cuda.Event(enable_timing=True)
+        stop = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(steps):
+            step()
+        stop.record()
+        torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    log(f"[bench] {name}: {ms * 1e3:.1f} us/step; kernels {timer.result}")
+
+    flops, bytes_, producer_bytes = algorithmic(case)
+    prod_name = {0: "produce_large", 1: "produce_stream", 2: "produce_f32"}[plan["regime"]]
+    p_launches, p_ms = timer.result.get(prod_name, (0, float("nan")))
+    p_ms_per_call = p_ms / steps
+    avg_launch_ms = p_ms / max(1, p_launches)
+    hbm_bound = plan["regime"] == 1
+    if hbm_bound:
+        achieved = producer_bytes / (p_ms_per_call * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": None}
+        value = bytes_ / (ms * 1e-3) / 1e9
+        unit = "GB/s"
+    else:
+        peak = PEAK_TFLOPS[case.dtype]
+        achieved = flops / (p_ms_per_call * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                "frac": achieved / peak, "traffic": None}
+        value = flops / (ms * 1e-3) / 1e12
+        unit = "TFLOP/s"
+    roof["kernel"] = prod_name
+    roof["avg_launch_us"] = avg_launch_ms * 1e3
+    roof["launches_per_step"] = p_launches / steps
+
+    res = {
+        "value": value, "unit": unit, "ms_per_step": ms,
+        "tflops": flops / (ms * 1e-3) / 1e12, "gbs": bytes_ / (ms * 1e-3) / 1e9,
+        "frac_bf16_peak": flops / (ms * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"],
+        "frac_hbm": bytes_ / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "roofline": roof,
+        "kernels_ms_per_step": {k: v[1] / steps for k, v in timer.result.items()},
+        "workspace_bytes": plan["workspace_bytes"], "ring_bytes": plan["ring_bytes"],
+        "d_expanded_x_fp32_bytes": case.M * case.K * 4,
+        "plan": plan,
+        "dtype": case.dtype,
+        "config": {"workload": name, "batch": case.batch, "topk": case.topk, "M": case.M,
+                   "G": case.G, "G_nonempty": int(np.count_nonzero(case.group_list)),
+                   "K": case.K, "N": case.N, "row_idx_type": case.row_idx_type,
+                   "algorithmic_bytes": bytes_, "flops": flops},
+    }
+    if cpu_baseline:
+        res["cpu_baseline"] = oracle_baseline(case, unit, log)
+    return res
+
+
+def oracle_baseline(case, unit, log):
+    """The oracle, as it stands, on a bounded sample of the workload."""
+    import numpy as np
+
+    import oracle
+    threads = oracle.default_threads()
+    # tokens whose full d_x rows the sample computes: all of a small batch,
+    # else a prefix sized for roughly 10-30 s of CPU work
+    n_tok = case.batch if case.M * case.N * case.K <= 8e9 else 48
+    toks = np.arange(n_tok, dtype=np.int64)
+    t0 = time.time()
+    oracle.case_dx_tokens(case, toks, nthreads=threads)
+    dt = time.time() - t0
+    rows = n_tok * case.topk
+    s = {"f32": 4, "f16": 2, "bf16": 2}[case.dtype]
+    if unit == "GB/s":
+        # the sample reads the d_y rows of its tokens and the weights of the experts they hit
+        experts = set()
+        off = np.concatenate([[0], np.cumsum(case.group_list)])
+        inv = np.empty(case.M, dtype=np.int64)
+        if case.row_idx_type == 0:
+            inv[case.eri] = np.arange(case.M)
+        else:
+            inv = case.eri
+        for p in range(n_tok * case.topk):
+            experts.add(int(np.searchsorted(off, inv[p], side="right") - 1))
+        b = rows * case.N * s + len(experts) * case.K * case.N * s + 4 * n_tok * case.K
+        val = b / dt / 1e9
+    else:
+        val = 2.0 * rows * case.N * case.K / dt / 1e12
+    log(f"[bench] oracle sample: {n_tok} tokens in {dt:.1f}s on {threads} threads")
+    return {"value": val, "unit": unit, "cores": threads, "kind": "oracle",
+            "seconds": dt,
+            "sample": f"d_x rows of tokens 0..{n_tok - 1} ({rows} expanded rows, all K columns) "
+                      f"of the same inputs"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="decode_bf16")
+    ap.add_argument("--no-large", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not supported",
+              file=sys.stderr)
+        return 2
+
+    def log(msg):
+        print(msg, file=sys.stderr, flush=True)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    primary = measure(args.workload, args.steps, args.warmup, not args.no_cpu_baseline, log)
+    line = {
+        "metric": METRIC,
+        "value": primary["value"], "unit": primary["unit"], "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": primary["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": primary["dtype"], "data": "synthetic",
+        "config": primary["config"],
+        "roofline": primary["roofline"],
+    }
+    if "cpu_baseline" in primary:
+        line["cpu_baseline"] = primary["cpu_baseline"]
+    line["detail"] = {k: primary[k] for k in ("tflops", "gbs", "frac_bf16_peak", "frac_hbm",
+                                              "kernels_ms_per_step", "workspace_bytes", "ring_bytes",
+                                              "d_expanded_x_fp32_bytes", "plan")}
+    if not args.no_large and args.workload != "large_f16":
+        large = measure("large_f16", max(5, args.steps // 2), args.warmup,
+                        not args.no_cpu_baseline, log)
+        line["large"] = {k: large[k] for k in ("value", "unit", "ms_per_step", "tflops", "gbs",
+                                               "frac_bf16_peak", "roofline", "kernels_ms_per_step",
+                                               "workspace_bytes", "ring_bytes",
+                                               "d_expanded_x_fp32_bytes", "config", "dtype")}
+        if "cpu_baseline" in large:
+            line["large"]["cpu_baseline"] = large["cpu_baseline"]
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

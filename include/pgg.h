@@ -1,0 +1,189 @@
+/*
+ * pgg.h — C ABI of the MI355X (gfx950) fused MoE backward that produces d_x.
+ *
+ * The operation (MoeInitRoutingGroupedMatmulGrad design page, §数学定义和公式):
+ *
+ *     d_x[b,k] = sum over expanded rows i with p(i) / topK == b
+ *                of  sum_n d_y[i,n] * W[g(i),k,n]
+ *
+ * i.e. the grouped-matmul gradient d_y · Wᵀ (Step 1) fused with the routing
+ * scatter-add back to the tokens (Step 2).  The [M,K] intermediate is never
+ * stored: fp32 tiles go through a workspace ring whose size does not depend
+ * on M, and a consumer stage adds them into d_x in a fixed order with no
+ * floating-point atomics, so repeated calls give bit-identical results.
+ *
+ * Two-phase use, as in the page's aclnn interface (§2.2.2): ask for the
+ * workspace size from the shapes alone, allocate it, then call the execute
+ * entry point.  The library never allocates, frees or synchronises inside
+ * pgg_moe_dx; it only enqueues kernels on the caller's stream.
+ *
+ * Thread safety: every entry point except the timing hooks is reentrant.
+ * Calls that share a workspace must be ordered by the caller (same stream or
+ * explicit events).
+ */
+#ifndef PGG_H
+#define PGG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of grad_y and weight (§1.2 I/O table: FLOAT / FLOAT16 / BF16). */
+typedef enum { PGG_F32 = 0, PGG_F16 = 1, PGG_BF16 = 2 } pgg_dtype;
+
+/* Host-side status of every entry point. */
+typedef enum {
+  PGG_OK = 0,
+  PGG_ERR_INVALID_ARG = 1,          /* a constraint of §1.2 / §2.3 is violated, or a NULL pointer */
+  PGG_ERR_UNSUPPORTED = 2,          /* valid per the page but beyond this build (e.g. M >= 2^31) */
+  PGG_ERR_WORKSPACE_TOO_SMALL = 3,  /* workspace_bytes below pgg_moe_dx_workspace_size */
+  PGG_ERR_HIP = 4,                  /* a HIP runtime call failed */
+  PGG_ERR_MISALIGNED = 5            /* workspace pointer not 256-byte aligned */
+} pgg_status;
+
+/* Data-dependent errors found on the device (read with
+ * pgg_moe_dx_read_device_error).  When one is set, d_x is unspecified. */
+typedef enum {
+  PGG_DEV_OK = 0,
+  PGG_DEV_GROUP_NEGATIVE = 1,       /* group_list[g] < 0; detail = g */
+  PGG_DEV_GROUP_SUM = 2,            /* sum(group_list) != M; detail = the sum (clamped to >= 0) */
+  PGG_DEV_INDEX_RANGE = 3,          /* expanded_row_idx[t] outside [0, M); detail = t */
+  PGG_DEV_INDEX_DUP = 4             /* expanded_row_idx is not a permutation; detail = a repeated value */
+} pgg_device_error;
+
+/*
+ * Problem descriptor.  All sizes are element counts; every tensor is dense
+ * and row-major (last index fastest).
+ *
+ *   grad_y            [grad_y_rows = M, grad_y_cols = N]          dtype
+ *   weight            [weight_groups = G, weight_rows = K, weight_cols = N]  dtype
+ *   expanded_row_idx  [idx_len = L]                                int64
+ *   group_list        [group_list_len = G]                         int64
+ *   grad_x (output)   [batch, K]                                   float32, always
+ *
+ * Constraints checked on the host (§1.2 constraints table, §2.3.3 checks):
+ * grad_y_cols == weight_cols; group_list_len == weight_groups; topk > 0;
+ * batch > 0; row_idx_type in {0, 1}; grad_y_dtype == weight_dtype; and
+ * L == M == batch * topk (the page bounds L by batch <= L <= batch*topK and
+ * L >= M, which with M = batch*topK leaves only L == M).
+ *
+ * row_idx_type (§1.2 notes): 0 = gather, expanded_row_idx[i] is the original
+ * position p = b*topK + j of expanded row i; 1 = scatter,
+ * expanded_row_idx[p] is the expanded row of original position p.
+ * group_list holds per-expert row counts (not a cumulative sum); expert g
+ * owns the expanded rows [sum_{h<g} group_list[h], sum_{h<=g} group_list[h]).
+ */
+typedef struct {
+  int64_t grad_y_rows, grad_y_cols;
+  int64_t weight_groups, weight_rows, weight_cols;
+  int64_t idx_len;
+  int64_t group_list_len;
+  int64_t batch, topk;
+  int32_t row_idx_type;
+  int32_t grad_y_dtype;   /* pgg_dtype */
+  int32_t weight_dtype;   /* pgg_dtype */
+  int32_t reserved;       /* must be 0 */
+} pgg_moe_dx_desc;
+
+/*
+ * Workspace size in bytes for a descriptor (host only; shapes only; no HIP
+ * call).  Returns PGG_ERR_INVALID_ARG / PGG_ERR_UNSUPPORTED for descriptors
+ * pgg_moe_dx would reject.  The size does not grow with M·K: it holds
+ * O(M + G) integer index tables plus a fixed-size fp32 tile ring.
+ */
+pgg_status pgg_moe_dx_workspace_size(const pgg_moe_dx_desc* desc, size_t* bytes);
+
+/*
+ * Enqueue the fused backward on `stream` (asynchronous; no host sync).
+ *
+ * grad_y, weight, expanded_row_idx, group_list: device pointers, read only.
+ * grad_x: device pointer to batch*K floats; fully overwritten (no pre-zeroing
+ *   needed).  It must not alias any input or the workspace.
+ * workspace: device pointer, 256-byte aligned, at least the queried size;
+ *   owned by the caller; its contents on entry are ignored.
+ *
+ * Host-checkable violations return a status before anything is enqueued.
+ * Data-dependent violations (negative count, sum != M, index out of range,
+ * index not a permutation) are recorded in the workspace; read them with
+ * pgg_moe_dx_read_device_error.  Empty experts' weight slices are never read.
+ */
+pgg_status pgg_moe_dx(const pgg_moe_dx_desc* desc, const void* grad_y, const void* weight,
+                      const int64_t* expanded_row_idx, const int64_t* group_list,
+                      float* grad_x, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream);
+
+/*
+ * Read the device error word of the last pgg_moe_dx that used `workspace`.
+ * Synchronises `stream`.  *code receives a pgg_device_error; *detail its
+ * detail value (may be NULL).  When several violations exist, the one with
+ * the smallest (code, detail) is reported, so the report is deterministic.
+ */
+pgg_status pgg_moe_dx_read_device_error(const void* workspace, hipStream_t stream,
+                                        int32_t* code, int64_t* detail);
+
+/*
+ * Copy the index tables the last call built into host arrays (tests only;
+ * synchronises `stream`).  inv_host[p] (length M) = expanded row of original
+ * position p; ori_host[i] (length M) = original position of expanded row i.
+ * Either pointer may be NULL.
+ */
+pgg_status pgg_moe_dx_debug_tables(const pgg_moe_dx_desc* desc, const void* workspace,
+                                   hipStream_t stream, int32_t* inv_host, int32_t* ori_host);
+
+/*
+ * The m-tile table the last call built (tests only; synchronises `stream`):
+ * tiles_host receives up to max_tiles entries of 3 int32 (expert, first
+ * expanded row, row count), in expert order, empty experts contributing none;
+ * *n_tiles the number of tiles.
+ */
+pgg_status pgg_moe_dx_debug_tiles(const pgg_moe_dx_desc* desc, const void* workspace,
+                                  hipStream_t stream, int32_t* tiles_host, int32_t max_tiles,
+                                  int32_t* n_tiles);
+
+/* Execution plan the library picks for a descriptor (host only, for reports). */
+typedef struct {
+  int32_t regime;          /* 0 = large-M MFMA tiles, 1 = weight-streaming (small M), 2 = fp32 */
+  int32_t block_m, block_n;/* output tile: expanded rows x output columns */
+  int32_t tiles_per_chunk; /* m-tiles whose rows share one ring buffer */
+  int32_t max_tiles;       /* upper bound on m-tiles: ceil(M/block_m) + G */
+  int32_t max_chunks;      /* chunks enqueued per call */
+  int32_t ring_rows;       /* rows of one ring buffer */
+  int32_t fused_prep;      /* 1 when index preparation runs as one workgroup */
+  size_t ring_bytes;       /* fp32 ring */
+  size_t table_bytes;      /* index / tile tables and header */
+  size_t workspace_bytes;  /* total, as returned by pgg_moe_dx_workspace_size */
+} pgg_plan;
+
+pgg_status pgg_moe_dx_plan(const pgg_moe_dx_desc* desc, pgg_plan* plan);
+
+/*
+ * Kernel timing hook (benchmarks).  Between pgg_timing_begin and
+ * pgg_timing_end, pgg_moe_dx records a HIP event on its stream before and
+ * after every kernel it launches.  pgg_timing_begin creates `capacity` event
+ * pairs (it allocates; never use it where allocation is forbidden) and
+ * pgg_timing_end waits for them and reports, per kernel name, the number of
+ * launches and their summed duration.  Not thread safe; one session at a
+ * time per process.
+ */
+typedef struct {
+  char name[32];
+  int32_t launches;
+  double total_ms;
+} pgg_kernel_time;
+
+pgg_status pgg_timing_begin(int32_t capacity);
+pgg_status pgg_timing_end(pgg_kernel_time* out, int32_t max_out, int32_t* n_out);
+
+const char* pgg_status_string(pgg_status status);
+const char* pgg_device_error_string(int32_t code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PGG_H */

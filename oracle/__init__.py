@@ -74,7 +74,9 @@ def lib():
         L.orc_dex.argtypes = [PP, vp, vp, vp, ctypes.c_int]
         L.orc_scatter.argtypes = [PP, vp, vp, vp, i32, vp, vp, vp]
         L.orc_dx_tokens.argtypes = [PP, vp, i64, vp, vp, vp, ctypes.c_int]
-        for f in ("orc_check", "orc_offsets", "orc_index", "orc_dex", "orc_scatter", "orc_dx_tokens"):
+        L.orc_colsum.argtypes = [PP, vp, i64, vp, vp, ctypes.c_int]
+        for f in ("orc_check", "orc_offsets", "orc_index", "orc_dex", "orc_scatter", "orc_dx_tokens",
+                  "orc_colsum"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -195,6 +197,25 @@ def moe_dx_tokens(grad_y, weight, eri, group_list, batch, topk, row_idx_type, dt
     if rc:
         raise OracleError(rc, "tokens")
     return dx32, dx64, absdot
+
+
+def colsum(grad_y, weight, eri, group_list, batch, topk, row_idx_type, dtype, cols, *,
+           nthreads=None):
+    """(sum over all tokens of d_x[:, k], matching sum of |terms|) for k in cols, in double."""
+    pr, keep = _problem(grad_y, weight, eri, group_list, batch, topk, row_idx_type, dtype)
+    cols = np.ascontiguousarray(cols, dtype=np.int64)
+    s = np.empty(cols.shape[0], dtype=np.float64)
+    a = np.empty(cols.shape[0], dtype=np.float64)
+    rc = lib().orc_colsum(ctypes.byref(pr), cols.ctypes.data, cols.shape[0], s.ctypes.data,
+                          a.ctypes.data, nthreads or default_threads())
+    if rc:
+        raise OracleError(rc, "colsum")
+    return s, a
+
+
+def case_colsum(case, cols, **kw):
+    return colsum(case.grad_y, case.weight, case.eri, case.group_list, case.batch, case.topk,
+                  case.row_idx_type, case.dtype, cols, **kw)
 
 
 def case_dx(case, mode=SLOT, **kw):

@@ -392,3 +392,76 @@ int orc_dx_tokens(const orc_problem* pr, const int64_t* tokens, int64_t ntok,
   free(off); free(ori); free(inv);
   return rc;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Column sums over every expanded row, for selected output columns          */
+/* ------------------------------------------------------------------------ */
+
+/* For each listed column k: colsum[t] = sum_i sum_n d_y[i,n] * W[g(i),k,n]
+ * and colabs[t] = the same sum of |terms|, both in double.  Step 2 only
+ * regroups the rows by token, so the sum over all tokens of d_x[:, k] equals
+ * this sum over all expanded rows of d_expanded_x[:, k] (the column-sum
+ * invariant); it holds at any size and touches every row. */
+typedef struct {
+  const orc_problem* pr;
+  const int64_t* off;
+  const int64_t* cols;
+  int64_t ncols;
+  double* sum;   /* [nthreads][ncols] partials */
+  double* asum;
+  int64_t begin, end;
+} colsum_work_t;
+
+static void* colsum_worker(void* arg) {
+  colsum_work_t* w = (colsum_work_t*)arg;
+  const orc_problem* pr = w->pr;
+  for (int64_t i = w->begin; i < w->end; ++i) {
+    int64_t g = expert_of_row(pr->G, w->off, i);
+    for (int64_t t = 0; t < w->ncols; ++t) {
+      const int64_t k = w->cols[t];
+      double s = 0.0, a = 0.0;
+      for (int64_t n = 0; n < pr->N; ++n) {
+        double y = load_elem(pr->dtype, pr->grad_y, i * pr->N + n);
+        double x = load_elem(pr->dtype, pr->weight, (g * pr->K + k) * pr->N + n);
+        s += y * x;
+        a += fabs(y) * fabs(x);
+      }
+      w->sum[t] += s;
+      w->asum[t] += a;
+    }
+  }
+  return NULL;
+}
+
+int orc_colsum(const orc_problem* pr, const int64_t* cols, int64_t ncols, double* colsum,
+               double* colabs, int nthreads) {
+  int64_t* off = (int64_t*)malloc(sizeof(int64_t) * (size_t)(pr->G + 1));
+  if (!off) return ORC_ERR_ALLOC;
+  int rc = orc_offsets(pr->G, pr->group_list, pr->M, off);
+  if (rc) { free(off); return rc; }
+  for (int64_t t = 0; t < ncols; ++t)
+    if (cols[t] < 0 || cols[t] >= pr->K) { free(off); return ORC_ERR_SHAPE; }
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > pr->M) nthreads = (int)pr->M;
+  pthread_t* th = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));
+  colsum_work_t* w = (colsum_work_t*)calloc((size_t)nthreads, sizeof(colsum_work_t));
+  double* part = (double*)calloc((size_t)nthreads * (size_t)ncols * 2, sizeof(double));
+  if (!th || !w || !part) { free(off); free(th); free(w); free(part); return ORC_ERR_ALLOC; }
+  for (int t = 0; t < nthreads; ++t) {
+    w[t].pr = pr; w[t].off = off; w[t].cols = cols; w[t].ncols = ncols;
+    w[t].sum = part + (size_t)t * (size_t)ncols * 2;
+    w[t].asum = w[t].sum + ncols;
+    w[t].begin = pr->M * t / nthreads;
+    w[t].end = pr->M * (t + 1) / nthreads;
+    pthread_create(&th[t], NULL, colsum_worker, &w[t]);
+  }
+  for (int t = 0; t < nthreads; ++t) pthread_join(th[t], NULL);
+  for (int64_t c = 0; c < ncols; ++c) {
+    double s = 0.0, a = 0.0;
+    for (int t = 0; t < nthreads; ++t) { s += w[t].sum[c]; a += w[t].asum[c]; }
+    colsum[c] = s;
+    if (colabs) colabs[c] = a;
+  }
+  free(off); free(th); free(w); free(part);
+  return ORC_OK;
+}

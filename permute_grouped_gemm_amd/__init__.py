@@ -1,0 +1,258 @@
+"""MI355X (gfx950) fused MoE backward producing d_x — Python binding.
+
+A thin ctypes layer over ``libpgg.so`` (built from ``csrc/`` by
+``python -m permute_grouped_gemm_amd.build``).  It only marshals arguments:
+PyTorch provides device memory and the current stream, and every step of the
+computation runs in the library's HIP kernels.  There is no CPU fallback: if
+the library is missing, importing the entry points raises.
+
+    d_x = moe_dx(grad_y, weight, expanded_row_idx, group_list, batch, topk, row_idx_type)
+
+computes, for the MoeInitRoutingGroupedMatmulGrad operator (design page,
+§数学定义和公式), d_x[b,k] = sum over expanded rows i of token b of
+sum_n grad_y[i,n] * weight[g(i),k,n], returned as float32 [batch, K].
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = [
+    "moe_dx", "workspace_size", "plan", "read_device_error", "debug_tables", "debug_tiles",
+    "KernelTimer", "PggError", "lib", "LIB_PATH", "HEADER_PATH",
+]
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libpgg.so")
+HEADER_PATH = os.path.join(os.path.dirname(PKG), "include", "pgg.h")
+
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE_TOO_SMALL, ERR_HIP, ERR_MISALIGNED = range(6)
+DEV_OK, DEV_GROUP_NEGATIVE, DEV_GROUP_SUM, DEV_INDEX_RANGE, DEV_INDEX_DUP = range(5)
+DTYPE_CODE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+
+
+class Desc(ctypes.Structure):
+    _fields_ = [
+        ("grad_y_rows", ctypes.c_int64), ("grad_y_cols", ctypes.c_int64),
+        ("weight_groups", ctypes.c_int64), ("weight_rows", ctypes.c_int64),
+        ("weight_cols", ctypes.c_int64), ("idx_len", ctypes.c_int64),
+        ("group_list_len", ctypes.c_int64), ("batch", ctypes.c_int64), ("topk", ctypes.c_int64),
+        ("row_idx_type", ctypes.c_int32), ("grad_y_dtype", ctypes.c_int32),
+        ("weight_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
+    ]
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [
+        ("regime", ctypes.c_int32), ("block_m", ctypes.c_int32), ("block_n", ctypes.c_int32),
+        ("tiles_per_chunk", ctypes.c_int32), ("max_tiles", ctypes.c_int32),
+        ("max_chunks", ctypes.c_int32), ("ring_rows", ctypes.c_int32),
+        ("fused_prep", ctypes.c_int32), ("ring_bytes", ctypes.c_size_t),
+        ("table_bytes", ctypes.c_size_t), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+    def as_dict(self) -> dict:
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+
+class KernelTime(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 32), ("launches", ctypes.c_int32),
+                ("total_ms", ctypes.c_double)]
+
+
+class PggError(RuntimeError):
+    def __init__(self, status: int, where: str = ""):
+        msg = lib().pgg_status_string(status).decode() if _lib is not None else str(status)
+        super().__init__(f"{where}: {msg} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libpgg.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m permute_grouped_gemm_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        PD = ctypes.POINTER(Desc)
+        L.pgg_moe_dx_workspace_size.argtypes = [PD, ctypes.POINTER(sz)]
+        L.pgg_moe_dx.argtypes = [PD, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.pgg_moe_dx_read_device_error.argtypes = [vp, vp, ctypes.POINTER(i32), ctypes.POINTER(i64)]
+        L.pgg_moe_dx_debug_tables.argtypes = [PD, vp, vp, vp, vp]
+        L.pgg_moe_dx_debug_tiles.argtypes = [PD, vp, vp, vp, i32, ctypes.POINTER(i32)]
+        L.pgg_moe_dx_plan.argtypes = [PD, ctypes.POINTER(Plan)]
+        L.pgg_timing_begin.argtypes = [i32]
+        L.pgg_timing_end.argtypes = [ctypes.POINTER(KernelTime), i32, ctypes.POINTER(i32)]
+        L.pgg_status_string.argtypes = [ctypes.c_int]
+        L.pgg_status_string.restype = ctypes.c_char_p
+        L.pgg_device_error_string.argtypes = [i32]
+        L.pgg_device_error_string.restype = ctypes.c_char_p
+        for f in ("pgg_moe_dx_workspace_size", "pgg_moe_dx", "pgg_moe_dx_read_device_error",
+                  "pgg_moe_dx_debug_tables", "pgg_moe_dx_debug_tiles", "pgg_moe_dx_plan",
+                  "pgg_timing_begin", "pgg_timing_end"):
+            getattr(L, f).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def header_functions() -> list:
+    """Names of the functions include/pgg.h declares."""
+    with open(HEADER_PATH) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(pgg_\w+)\s*\(", text, re.M)))
+
+
+def _check(status: int, where: str):
+    if status != OK:
+        raise PggError(status, where)
+
+
+def make_desc(grad_y_shape, weight_shape, idx_len, group_list_len, batch, topk, row_idx_type,
+              grad_y_dtype, weight_dtype) -> Desc:
+    if len(grad_y_shape) != 2 or len(weight_shape) != 3:
+        raise PggError(ERR_INVALID_ARG, "rank")
+    d = Desc()
+    d.grad_y_rows, d.grad_y_cols = (int(v) for v in grad_y_shape)
+    d.weight_groups, d.weight_rows, d.weight_cols = (int(v) for v in weight_shape)
+    d.idx_len = int(idx_len)
+    d.group_list_len = int(group_list_len)
+    d.batch = int(batch)
+    d.topk = int(topk)
+    d.row_idx_type = int(row_idx_type)
+    d.grad_y_dtype = grad_y_dtype
+    d.weight_dtype = weight_dtype
+    d.reserved = 0
+    return d
+
+
+def _desc_from_tensors(grad_y, weight, eri, group_list, batch, topk, row_idx_type) -> Desc:
+    if eri.dim() != 1 or group_list.dim() != 1:
+        raise PggError(ERR_INVALID_ARG, "rank")
+    if eri.dtype != torch.int64 or group_list.dtype != torch.int64:
+        raise PggError(ERR_INVALID_ARG, "index dtype")
+    gy = DTYPE_CODE.get(grad_y.dtype, -1)
+    wt = DTYPE_CODE.get(weight.dtype, -1)
+    return make_desc(grad_y.shape, weight.shape, eri.shape[0], group_list.shape[0], batch, topk,
+                     row_idx_type, gy, wt)
+
+
+def workspace_size_desc(d: Desc) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().pgg_moe_dx_workspace_size(ctypes.byref(d), ctypes.byref(n)), "workspace_size")
+    return n.value
+
+
+def plan_desc(d: Desc) -> dict:
+    p = Plan()
+    _check(lib().pgg_moe_dx_plan(ctypes.byref(d), ctypes.byref(p)), "plan")
+    return p.as_dict()
+
+
+def workspace_size(grad_y, weight, expanded_row_idx, group_list, batch, topk, row_idx_type=0) -> int:
+    return workspace_size_desc(_desc_from_tensors(grad_y, weight, expanded_row_idx, group_list,
+                                                  batch, topk, row_idx_type))
+
+
+def plan(grad_y, weight, expanded_row_idx, group_list, batch, topk, row_idx_type=0) -> dict:
+    return plan_desc(_desc_from_tensors(grad_y, weight, expanded_row_idx, group_list, batch, topk,
+                                        row_idx_type))
+
+
+def _stream_handle(stream) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return int(s.cuda_stream)
+
+
+def moe_dx(grad_y: torch.Tensor, weight: torch.Tensor, expanded_row_idx: torch.Tensor,
+           group_list: torch.Tensor, batch: int, topk: int, row_idx_type: int = 0, *,
+           out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+           stream=None) -> torch.Tensor:
+    """Fused backward: float32 d_x [batch, K] (asynchronous on the current stream).
+
+    grad_y [M, N] and weight [G, K, N] share one of float32 / float16 /
+    bfloat16; expanded_row_idx [M] and group_list [G] are int64; all on one
+    GPU.  ``workspace`` (uint8, at least ``workspace_size(...)`` bytes,
+    256-byte aligned) and ``out`` may be passed to avoid allocations."""
+    d = _desc_from_tensors(grad_y, weight, expanded_row_idx, group_list, batch, topk, row_idx_type)
+    for t in (grad_y, weight, expanded_row_idx, group_list):
+        if not t.is_cuda or not t.is_contiguous():
+            raise PggError(ERR_INVALID_ARG, "inputs must be contiguous GPU tensors")
+    need = workspace_size_desc(d)
+    dev = grad_y.device
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if out is None:
+        out = torch.empty((int(batch), int(weight.shape[1])), dtype=torch.float32, device=dev)
+    if out.dtype != torch.float32 or not out.is_contiguous() or tuple(out.shape) != (int(batch), int(weight.shape[1])):
+        raise PggError(ERR_INVALID_ARG, "out must be a contiguous float32 [batch, K] tensor")
+    st = lib().pgg_moe_dx(ctypes.byref(d), grad_y.data_ptr(), weight.data_ptr(),
+                          expanded_row_idx.data_ptr(), group_list.data_ptr(), out.data_ptr(),
+                          workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                          _stream_handle(stream))
+    _check(st, "pgg_moe_dx")
+    return out
+
+
+def read_device_error(workspace: torch.Tensor, stream=None) -> Tuple[int, int]:
+    code = ctypes.c_int32()
+    detail = ctypes.c_int64()
+    _check(lib().pgg_moe_dx_read_device_error(workspace.data_ptr(), _stream_handle(stream),
+                                              ctypes.byref(code), ctypes.byref(detail)),
+           "read_device_error")
+    return code.value, detail.value
+
+
+def debug_tables(grad_y, weight, expanded_row_idx, group_list, batch, topk, row_idx_type,
+                 workspace, stream=None):
+    """(inv, ori) int32 host tensors built by the last call on ``workspace``."""
+    d = _desc_from_tensors(grad_y, weight, expanded_row_idx, group_list, batch, topk, row_idx_type)
+    M = d.grad_y_rows
+    inv = torch.empty(M, dtype=torch.int32)
+    ori = torch.empty(M, dtype=torch.int32)
+    _check(lib().pgg_moe_dx_debug_tables(ctypes.byref(d), workspace.data_ptr(),
+                                         _stream_handle(stream), inv.data_ptr(), ori.data_ptr()),
+           "debug_tables")
+    return inv, ori
+
+
+def debug_tiles(grad_y, weight, expanded_row_idx, group_list, batch, topk, row_idx_type,
+                workspace, stream=None):
+    """m-tile table [(expert, first row, rows)] built by the last call on ``workspace``."""
+    d = _desc_from_tensors(grad_y, weight, expanded_row_idx, group_list, batch, topk, row_idx_type)
+    cap = plan_desc(d)["max_tiles"]
+    buf = torch.empty(3 * cap, dtype=torch.int32)
+    n = ctypes.c_int32()
+    _check(lib().pgg_moe_dx_debug_tiles(ctypes.byref(d), workspace.data_ptr(), _stream_handle(stream),
+                                        buf.data_ptr(), cap, ctypes.byref(n)), "debug_tiles")
+    return buf[: 3 * n.value].reshape(-1, 3)
+
+
+class KernelTimer:
+    """Per-kernel HIP-event timing of pgg_moe_dx calls made inside the block."""
+
+    def __init__(self, capacity: int = 4096):
+        self.capacity = capacity
+        self.result = {}
+
+    def __enter__(self):
+        _check(lib().pgg_timing_begin(self.capacity), "timing_begin")
+        return self
+
+    def __exit__(self, *exc):
+        out = (KernelTime * 64)()
+        n = ctypes.c_int32()
+        st = lib().pgg_timing_end(out, 64, ctypes.byref(n))
+        self.result = {out[i].name.decode(): (out[i].launches, out[i].total_ms)
+                       for i in range(min(n.value, 64))}
+        if exc[0] is None:
+            _check(st, "timing_end")
+        return False

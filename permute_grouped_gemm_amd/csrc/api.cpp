@@ -1,0 +1,277 @@
+// C ABI of the fused MoE d_x backward (declared in include/pgg.h).
+//
+// The execute call validates the descriptor on the host, lays out the
+// workspace, and enqueues on the caller's stream:
+//   1. index preparation (one workgroup for small M, three grid-wide passes
+//      otherwise): group offsets, the m-tile table, inv/ori tables, checks;
+//   2. for every chunk of m-tiles: the MFMA producer, which writes the
+//      chunk's fp32 rows into the ring, then the ordered consumer, which adds
+//      them into d_x.
+// Stream order carries every dependency; there is no host synchronisation
+// and no allocation on this path.
+#include <stdio.h>
+#include <string.h>
+
+#include <vector>
+
+#include "pgg_internal.h"
+
+using namespace pgg;
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// timing hook
+// ---------------------------------------------------------------------------
+struct TimingSession {
+  bool active = false;
+  std::vector<hipEvent_t> start, stop;
+  std::vector<const char*> names;
+  int used = 0;
+  bool overflow = false;
+};
+
+TimingSession g_timing;
+
+struct TimedLaunch {
+  const char* name;
+  hipStream_t stream;
+  int idx = -1;
+  TimedLaunch(const char* n, hipStream_t s) : name(n), stream(s) {
+    if (!g_timing.active) return;
+    if (g_timing.used >= static_cast<int>(g_timing.start.size())) {
+      g_timing.overflow = true;
+      return;
+    }
+    idx = g_timing.used++;
+    g_timing.names[idx] = name;
+    (void)hipEventRecord(g_timing.start[idx], stream);
+  }
+  ~TimedLaunch() {
+    if (idx >= 0) (void)hipEventRecord(g_timing.stop[idx], stream);
+  }
+};
+
+bool is_aligned(const void* ptr, size_t a) { return reinterpret_cast<uintptr_t>(ptr) % a == 0; }
+
+size_t elem_size(int32_t dtype) { return dtype == PGG_F32 ? 4 : 2; }
+
+}  // namespace
+
+extern "C" {
+
+pgg_status pgg_moe_dx_workspace_size(const pgg_moe_dx_desc* desc, size_t* bytes) {
+  if (!bytes) return PGG_ERR_INVALID_ARG;
+  Plan p;
+  const pgg_status st = make_plan(desc, &p);
+  if (st != PGG_OK) return st;
+  *bytes = p.total;
+  return PGG_OK;
+}
+
+pgg_status pgg_moe_dx_plan(const pgg_moe_dx_desc* desc, pgg_plan* out) {
+  if (!out) return PGG_ERR_INVALID_ARG;
+  Plan p;
+  const pgg_status st = make_plan(desc, &p);
+  if (st != PGG_OK) return st;
+  out->regime = p.regime;
+  out->block_m = p.bm;
+  out->block_n = p.bn;
+  out->tiles_per_chunk = p.tc;
+  out->max_tiles = p.max_tiles;
+  out->max_chunks = p.max_chunks;
+  out->ring_rows = p.ring_rows;
+  out->fused_prep = p.fused_prep ? 1 : 0;
+  out->ring_bytes = p.ring_bytes;
+  out->table_bytes = p.table_bytes;
+  out->workspace_bytes = p.total;
+  return PGG_OK;
+}
+
+pgg_status pgg_moe_dx(const pgg_moe_dx_desc* desc, const void* grad_y, const void* weight,
+                      const int64_t* expanded_row_idx, const int64_t* group_list, float* grad_x,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  Plan p;
+  const pgg_status st = make_plan(desc, &p);
+  if (st != PGG_OK) return st;
+  if (!grad_y || !weight || !expanded_row_idx || !group_list || !grad_x || !workspace)
+    return PGG_ERR_INVALID_ARG;
+  if (workspace_bytes < p.total) return PGG_ERR_WORKSPACE_TOO_SMALL;
+  if (!is_aligned(workspace, kWorkspaceAlign)) return PGG_ERR_MISALIGNED;
+  if (!is_aligned(expanded_row_idx, 8) || !is_aligned(group_list, 8) || !is_aligned(grad_x, 4) ||
+      !is_aligned(grad_y, elem_size(p.dtype)) || !is_aligned(weight, elem_size(p.dtype)))
+    return PGG_ERR_MISALIGNED;
+
+  const bool aligned = is_aligned(grad_y, 16) && is_aligned(weight, 16) &&
+                       (size_t(p.N) * elem_size(p.dtype)) % 16 == 0;
+  const WsView w = ws_view(p, workspace);
+
+  hipError_t e = hipSuccess;
+  if (p.fused_prep) {
+    TimedLaunch t("prep_fused", stream);
+    e = launch_prep_fused(p, expanded_row_idx, group_list, w, stream);
+  } else {
+    {
+      TimedLaunch t("prep_groups", stream);
+      e = launch_prep_groups(p, group_list, w, stream);
+    }
+    if (e == hipSuccess) {
+      TimedLaunch t("prep_index", stream);
+      e = launch_prep_index(p, expanded_row_idx, w, stream);
+    }
+    if (e == hipSuccess) {
+      TimedLaunch t("prep_verify", stream);
+      e = launch_prep_verify(p, expanded_row_idx, w, stream);
+    }
+  }
+  const char* pname = produce_kernel_name(p);
+  for (int c = 0; c < p.max_chunks && e == hipSuccess; ++c) {
+    {
+      TimedLaunch t(pname, stream);
+      e = launch_produce(p, c, grad_y, weight, aligned, w, stream);
+    }
+    if (e != hipSuccess) break;
+    TimedLaunch t("consume", stream);
+    e = launch_consume(p, c, w, grad_x, stream);
+  }
+  return e == hipSuccess ? PGG_OK : PGG_ERR_HIP;
+}
+
+pgg_status pgg_moe_dx_read_device_error(const void* workspace, hipStream_t stream, int32_t* code,
+                                        int64_t* detail) {
+  if (!workspace || !code) return PGG_ERR_INVALID_ARG;
+  WsHeader h;
+  if (hipMemcpyAsync(&h, workspace, sizeof(h), hipMemcpyDeviceToHost, stream) != hipSuccess)
+    return PGG_ERR_HIP;
+  if (hipStreamSynchronize(stream) != hipSuccess) return PGG_ERR_HIP;
+  if (h.err == kNoError) {
+    *code = PGG_DEV_OK;
+    if (detail) *detail = 0;
+  } else {
+    *code = static_cast<int32_t>(h.err >> kErrShift);
+    if (detail) *detail = static_cast<int64_t>(h.err & kDetailMask);
+  }
+  return PGG_OK;
+}
+
+pgg_status pgg_moe_dx_debug_tables(const pgg_moe_dx_desc* desc, const void* workspace,
+                                   hipStream_t stream, int32_t* inv_host, int32_t* ori_host) {
+  Plan p;
+  const pgg_status st = make_plan(desc, &p);
+  if (st != PGG_OK) return st;
+  if (!workspace) return PGG_ERR_INVALID_ARG;
+  const WsView w = ws_view(p, const_cast<void*>(workspace));
+  const size_t bytes = sizeof(int32_t) * size_t(p.M);
+  if (inv_host && hipMemcpyAsync(inv_host, w.inv, bytes, hipMemcpyDeviceToHost, stream) != hipSuccess)
+    return PGG_ERR_HIP;
+  if (ori_host && hipMemcpyAsync(ori_host, w.ori, bytes, hipMemcpyDeviceToHost, stream) != hipSuccess)
+    return PGG_ERR_HIP;
+  return hipStreamSynchronize(stream) == hipSuccess ? PGG_OK : PGG_ERR_HIP;
+}
+
+pgg_status pgg_moe_dx_debug_tiles(const pgg_moe_dx_desc* desc, const void* workspace,
+                                  hipStream_t stream, int32_t* tiles_host, int32_t max_tiles,
+                                  int32_t* n_tiles) {
+  Plan p;
+  const pgg_status st = make_plan(desc, &p);
+  if (st != PGG_OK) return st;
+  if (!workspace || !n_tiles || (max_tiles > 0 && !tiles_host)) return PGG_ERR_INVALID_ARG;
+  const WsView w = ws_view(p, const_cast<void*>(workspace));
+  WsHeader h;
+  if (hipMemcpyAsync(&h, w.hdr, sizeof(h), hipMemcpyDeviceToHost, stream) != hipSuccess)
+    return PGG_ERR_HIP;
+  if (hipStreamSynchronize(stream) != hipSuccess) return PGG_ERR_HIP;
+  *n_tiles = h.n_tiles;
+  const int32_t n = h.n_tiles < max_tiles ? h.n_tiles : max_tiles;
+  if (n > 0) {
+    std::vector<MTile> t(static_cast<size_t>(n));
+    if (hipMemcpyAsync(t.data(), w.tiles, sizeof(MTile) * t.size(), hipMemcpyDeviceToHost, stream) !=
+        hipSuccess)
+      return PGG_ERR_HIP;
+    if (hipStreamSynchronize(stream) != hipSuccess) return PGG_ERR_HIP;
+    for (int32_t i = 0; i < n; ++i) {
+      tiles_host[3 * i + 0] = t[i].g;
+      tiles_host[3 * i + 1] = t[i].row0;
+      tiles_host[3 * i + 2] = t[i].rows;
+    }
+  }
+  return PGG_OK;
+}
+
+pgg_status pgg_timing_begin(int32_t capacity) {
+  if (capacity <= 0 || g_timing.active) return PGG_ERR_INVALID_ARG;
+  g_timing.start.assign(static_cast<size_t>(capacity), nullptr);
+  g_timing.stop.assign(static_cast<size_t>(capacity), nullptr);
+  g_timing.names.assign(static_cast<size_t>(capacity), nullptr);
+  for (int32_t i = 0; i < capacity; ++i) {
+    if (hipEventCreate(&g_timing.start[i]) != hipSuccess ||
+        hipEventCreate(&g_timing.stop[i]) != hipSuccess)
+      return PGG_ERR_HIP;
+  }
+  g_timing.used = 0;
+  g_timing.overflow = false;
+  g_timing.active = true;
+  return PGG_OK;
+}
+
+pgg_status pgg_timing_end(pgg_kernel_time* out, int32_t max_out, int32_t* n_out) {
+  if (!g_timing.active) return PGG_ERR_INVALID_ARG;
+  g_timing.active = false;
+  std::vector<pgg_kernel_time> acc;
+  pgg_status st = PGG_OK;
+  for (int i = 0; i < g_timing.used; ++i) {
+    if (hipEventSynchronize(g_timing.stop[i]) != hipSuccess) { st = PGG_ERR_HIP; break; }
+    float ms = 0.0f;
+    if (hipEventElapsedTime(&ms, g_timing.start[i], g_timing.stop[i]) != hipSuccess) {
+      st = PGG_ERR_HIP;
+      break;
+    }
+    size_t k = 0;
+    for (; k < acc.size(); ++k)
+      if (strncmp(acc[k].name, g_timing.names[i], sizeof(acc[k].name)) == 0) break;
+    if (k == acc.size()) {
+      pgg_kernel_time t{};
+      snprintf(t.name, sizeof(t.name), "%s", g_timing.names[i]);
+      acc.push_back(t);
+    }
+    acc[k].launches += 1;
+    acc[k].total_ms += ms;
+  }
+  for (size_t i = 0; i < g_timing.start.size(); ++i) {
+    if (g_timing.start[i]) (void)hipEventDestroy(g_timing.start[i]);
+    if (g_timing.stop[i]) (void)hipEventDestroy(g_timing.stop[i]);
+  }
+  g_timing.start.clear();
+  g_timing.stop.clear();
+  g_timing.names.clear();
+  const int32_t n = static_cast<int32_t>(acc.size());
+  if (n_out) *n_out = n;
+  for (int32_t i = 0; i < n && i < max_out && out; ++i) out[i] = acc[static_cast<size_t>(i)];
+  if (st == PGG_OK && g_timing.overflow) st = PGG_ERR_INVALID_ARG;
+  return st;
+}
+
+const char* pgg_status_string(pgg_status s) {
+  switch (s) {
+    case PGG_OK: return "ok";
+    case PGG_ERR_INVALID_ARG: return "invalid argument";
+    case PGG_ERR_UNSUPPORTED: return "unsupported problem size";
+    case PGG_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case PGG_ERR_HIP: return "HIP runtime error";
+    case PGG_ERR_MISALIGNED: return "misaligned pointer";
+  }
+  return "unknown status";
+}
+
+const char* pgg_device_error_string(int32_t code) {
+  switch (code) {
+    case PGG_DEV_OK: return "ok";
+    case PGG_DEV_GROUP_NEGATIVE: return "group_list has a negative count";
+    case PGG_DEV_GROUP_SUM: return "sum(group_list) != M";
+    case PGG_DEV_INDEX_RANGE: return "expanded_row_idx value outside [0, M)";
+    case PGG_DEV_INDEX_DUP: return "expanded_row_idx is not a permutation";
+  }
+  return "unknown device error";
+}
+
+}  // extern "C"

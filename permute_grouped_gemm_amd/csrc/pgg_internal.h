@@ -1,0 +1,112 @@
+// Internal definitions shared by the host planner, the C ABI and the HIP
+// kernels of the fused MoE d_x backward.  Not part of the public ABI.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "pgg.h"
+
+namespace pgg {
+
+// ---------------------------------------------------------------------------
+// Workspace header (offset 0).  `err` packs a device error as
+// (code << 48) | detail and is lowered with atomicMin, so the smallest
+// (code, detail) wins and the report does not depend on thread timing.
+// kNoError means no error.
+// ---------------------------------------------------------------------------
+constexpr unsigned long long kNoError = ~0ull;
+constexpr int kErrShift = 48;
+constexpr unsigned long long kDetailMask = (1ull << kErrShift) - 1;
+
+struct alignas(16) WsHeader {
+  unsigned long long err;
+  int32_t n_tiles;      // m-tiles actually produced by the group pass
+  int32_t reserved0;
+  int64_t reserved[6];
+};
+
+// One m-tile: up to block_m consecutive expanded rows of one expert.
+struct alignas(16) MTile {
+  int32_t g;
+  int32_t row0;   // first expanded row
+  int32_t rows;   // 1..block_m; 0 marks an unused slot
+  int32_t pad;
+};
+
+enum Regime : int32_t { kLarge = 0, kStream = 1, kF32 = 2 };
+
+// Workspace regions are aligned to 512 bytes, as the page's tiling aligns its
+// workspace regions (MoeInitRoutingGroupedMatmulGrad design, §2.4.3).
+constexpr size_t kRegionAlign = 512;
+constexpr size_t kWorkspaceAlign = 256;
+
+struct Plan {
+  // problem
+  int64_t M, N, G, K, batch, topk;
+  int32_t row_idx_type;
+  int32_t dtype;
+  // schedule
+  int32_t regime;
+  int32_t bm, bn;
+  int32_t tc;          // m-tiles per chunk
+  int32_t max_tiles;   // ceil(M/bm) + G
+  int32_t max_chunks;  // ceil(max_tiles / tc)
+  int32_t ring_rows;   // tc * bm
+  int32_t n_col_tiles; // ceil(K / bn)
+  bool fused_prep;
+  // layout (byte offsets into the workspace)
+  size_t off_header, off_offsets, off_tiles, off_chunks, off_inv, off_ori, off_ring, total;
+  size_t ring_bytes, table_bytes;
+};
+
+// Fills *plan from a descriptor; returns PGG_OK or the rejection status.
+pgg_status make_plan(const pgg_moe_dx_desc* desc, Plan* plan);
+
+// Views of the workspace regions.
+struct WsView {
+  WsHeader* hdr;
+  int64_t* offsets;     // [G+1]
+  MTile* tiles;         // [max_tiles]
+  int32_t* chunk_row0;  // [max_chunks+1]
+  int32_t* inv;         // [M]  original position -> expanded row
+  int32_t* ori;         // [M]  expanded row -> original position
+  float* ring;          // [ring_rows, K]
+};
+
+inline WsView ws_view(const Plan& p, void* ws) {
+  char* b = static_cast<char*>(ws);
+  WsView v;
+  v.hdr = reinterpret_cast<WsHeader*>(b + p.off_header);
+  v.offsets = reinterpret_cast<int64_t*>(b + p.off_offsets);
+  v.tiles = reinterpret_cast<MTile*>(b + p.off_tiles);
+  v.chunk_row0 = reinterpret_cast<int32_t*>(b + p.off_chunks);
+  v.inv = reinterpret_cast<int32_t*>(b + p.off_inv);
+  v.ori = reinterpret_cast<int32_t*>(b + p.off_ori);
+  v.ring = reinterpret_cast<float*>(b + p.off_ring);
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// Kernel launchers (each enqueues exactly one kernel).
+// ---------------------------------------------------------------------------
+hipError_t launch_prep_fused(const Plan& p, const int64_t* eri, const int64_t* group_list,
+                             const WsView& w, hipStream_t s);
+hipError_t launch_prep_groups(const Plan& p, const int64_t* group_list, const WsView& w,
+                              hipStream_t s);
+hipError_t launch_prep_index(const Plan& p, const int64_t* eri, const WsView& w, hipStream_t s);
+hipError_t launch_prep_verify(const Plan& p, const int64_t* eri, const WsView& w, hipStream_t s);
+
+// Producer: chunk c's m-tiles x all column tiles -> ring rows.
+hipError_t launch_produce(const Plan& p, int chunk, const void* grad_y, const void* weight,
+                          bool aligned, const WsView& w, hipStream_t s);
+
+// Consumer: ordered scatter-add of chunk c's ring rows into d_x.
+hipError_t launch_consume(const Plan& p, int chunk, const WsView& w, float* grad_x,
+                          hipStream_t s);
+
+const char* produce_kernel_name(const Plan& p);
+
+}  // namespace pgg

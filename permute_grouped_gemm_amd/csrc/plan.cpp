@@ -1,0 +1,111 @@
+// Host-side validation and workspace planning (shapes only; no HIP calls).
+//
+// Validation follows the constraints table of the MoeInitRoutingGroupedMatmulGrad
+// design page (§1.2) and its infershape checks (§2.3.3).  The schedule splits
+// the expert-ordered list of m-tiles into chunks whose fp32 output rows fit a
+// ring of bounded size, so the workspace does not grow with M·K.
+#include <stdlib.h>
+
+#include <algorithm>
+
+#include "pgg_internal.h"
+
+namespace pgg {
+
+namespace {
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Bound on the fp32 ring (bytes).  PGG_RING_MB overrides it for tuning; a
+// fixed setting gives fixed results.
+size_t ring_budget() {
+  const char* e = getenv("PGG_RING_MB");
+  if (e) {
+    long mb = strtol(e, nullptr, 10);
+    if (mb > 0) return static_cast<size_t>(mb) << 20;
+  }
+  return size_t(256) << 20;
+}
+
+struct TileShape { int bm, bn; };
+
+// Output tile per regime: large-M MFMA tiles, narrow tiles that spread the
+// weight stream over many workgroups when experts hold few rows, fp32 tiles.
+TileShape tile_shape(int32_t regime) {
+  switch (regime) {
+    case kLarge: return {256, 256};
+    case kStream: return {32, 128};
+    default: return {128, 128};
+  }
+}
+
+}  // namespace
+
+pgg_status make_plan(const pgg_moe_dx_desc* d, Plan* p) {
+  if (!d || !p) return PGG_ERR_INVALID_ARG;
+  const int64_t M = d->grad_y_rows, N = d->grad_y_cols;
+  const int64_t G = d->weight_groups, K = d->weight_rows;
+  if (d->reserved != 0) return PGG_ERR_INVALID_ARG;
+  if (d->topk <= 0 || d->batch <= 0) return PGG_ERR_INVALID_ARG;
+  if (d->row_idx_type != 0 && d->row_idx_type != 1) return PGG_ERR_INVALID_ARG;
+  if (d->grad_y_dtype != d->weight_dtype) return PGG_ERR_INVALID_ARG;
+  if (d->grad_y_dtype < PGG_F32 || d->grad_y_dtype > PGG_BF16) return PGG_ERR_INVALID_ARG;
+  if (N != d->weight_cols) return PGG_ERR_INVALID_ARG;
+  if (d->group_list_len != G) return PGG_ERR_INVALID_ARG;
+  if (G <= 0 || K <= 0 || N <= 0 || M <= 0) return PGG_ERR_INVALID_ARG;
+  if (d->topk > INT64_MAX / d->batch) return PGG_ERR_INVALID_ARG;
+  if (M != d->batch * d->topk) return PGG_ERR_INVALID_ARG;
+  const int64_t L = d->idx_len;
+  if (L < d->batch || L > d->batch * d->topk || L < M) return PGG_ERR_INVALID_ARG;
+  // Row indices are kept as int32 on the device; the page limits M to 2^31.
+  if (M >= (int64_t(1) << 31) - 1) return PGG_ERR_UNSUPPORTED;
+  if (G >= (int64_t(1) << 30) || K >= (int64_t(1) << 31) || N >= (int64_t(1) << 31))
+    return PGG_ERR_UNSUPPORTED;
+
+  Plan q{};
+  q.M = M; q.N = N; q.G = G; q.K = K; q.batch = d->batch; q.topk = d->topk;
+  q.row_idx_type = d->row_idx_type;
+  q.dtype = d->grad_y_dtype;
+  if (q.dtype == PGG_F32) {
+    q.regime = kF32;
+  } else if (M <= 64 * G) {
+    q.regime = kStream;   // on average at most 64 rows per expert: weight streaming dominates
+  } else {
+    q.regime = kLarge;
+  }
+  const TileShape ts = tile_shape(q.regime);
+  q.bm = ts.bm;
+  q.bn = ts.bn;
+  const int64_t max_tiles = (M + q.bm - 1) / q.bm + G;
+  if (max_tiles >= (int64_t(1) << 31)) return PGG_ERR_UNSUPPORTED;
+  q.max_tiles = static_cast<int32_t>(max_tiles);
+  const size_t per_tile = size_t(q.bm) * size_t(K) * sizeof(float);
+  int64_t tc = static_cast<int64_t>(ring_budget() / per_tile);
+  tc = std::max<int64_t>(1, std::min<int64_t>(tc, max_tiles));
+  // keep the consumer grid (ring rows x column blocks of 256) well inside 2^31 work-items
+  const int64_t col_blocks_worst = (K + 255) / 256;
+  while (tc > 1 && tc * q.bm * col_blocks_worst >= (int64_t(1) << 23)) tc /= 2;
+  if (int64_t(q.bm) * col_blocks_worst >= (int64_t(1) << 23)) return PGG_ERR_UNSUPPORTED;
+  q.tc = static_cast<int32_t>(tc);
+  q.max_chunks = static_cast<int32_t>((max_tiles + tc - 1) / tc);
+  q.ring_rows = q.tc * q.bm;
+  q.n_col_tiles = static_cast<int32_t>((K + q.bn - 1) / q.bn);
+  q.fused_prep = M <= 16384;
+
+  size_t off = 0;
+  q.off_header = off;   off = align_up(off + sizeof(WsHeader), kRegionAlign);
+  q.off_offsets = off;  off = align_up(off + sizeof(int64_t) * size_t(G + 1), kRegionAlign);
+  q.off_tiles = off;    off = align_up(off + sizeof(MTile) * size_t(q.max_tiles), kRegionAlign);
+  q.off_chunks = off;   off = align_up(off + sizeof(int32_t) * size_t(q.max_chunks + 1), kRegionAlign);
+  q.off_inv = off;      off = align_up(off + sizeof(int32_t) * size_t(M), kRegionAlign);
+  q.off_ori = off;      off = align_up(off + sizeof(int32_t) * size_t(M), kRegionAlign);
+  q.table_bytes = off;
+  q.off_ring = off;
+  q.ring_bytes = size_t(q.ring_rows) * size_t(K) * sizeof(float);
+  off = align_up(off + q.ring_bytes, kRegionAlign);
+  q.total = off;
+  *p = q;
+  return PGG_OK;
+}
+
+}  // namespace pgg

@@ -26,7 +26,9 @@ storage type is IEEE round-to-nearest-even.
 """
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
+import os
 from typing import Optional, Sequence
 
 import numpy as np
@@ -65,16 +67,42 @@ class Case:
 # rounding to storage types (input construction only)
 # ----------------------------------------------------------------------------
 
+_BLOCK = 1 << 22
+
+
+def _threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _blocks(n: int):
+    return [(s, min(n, s + _BLOCK)) for s in range(0, n, _BLOCK)]
+
+
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round float32 values to bfloat16 (RNE) and return the uint16 bit patterns."""
-    x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    nan = np.isnan(x)
-    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    r = r.astype(np.uint16)
-    if nan.any():
-        r[nan] = np.uint16(0x7FC0)
-    return r
+    flat = np.ascontiguousarray(x, dtype=np.float32).reshape(-1)
+    out = np.empty(flat.shape, dtype=np.uint16)
+
+    def work(se):
+        s, e = se
+        u = flat[s:e].view(np.uint32)
+        r = (u >> 16) & 1          # finite values: u + 0x7FFF + lsb stays below 2^32
+        r += 0x7FFF
+        r += u
+        r >>= 16
+        blk = r.astype(np.uint16)
+        nan = np.isnan(flat[s:e])
+        if nan.any():
+            blk[nan] = np.uint16(0x7FC0)
+        out[s:e] = blk
+
+    with concurrent.futures.ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(work, _blocks(flat.size)))
+    return out.reshape(np.shape(x))
 
 
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
@@ -86,7 +114,15 @@ def to_storage(x: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "f32":
         return np.ascontiguousarray(x, dtype=np.float32)
     if dtype == "f16":
-        return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16)
+        flat = np.ascontiguousarray(x, dtype=np.float32).reshape(-1)
+        out = np.empty(flat.shape, dtype=np.float16)
+
+        def work(se):
+            out[se[0]:se[1]] = flat[se[0]:se[1]].astype(np.float16)
+
+        with concurrent.futures.ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(work, _blocks(flat.size)))
+        return out.reshape(np.shape(x))
     if dtype == "bf16":
         return f32_to_bf16_bits(x)
     raise ValueError(dtype)
@@ -156,14 +192,26 @@ def assemble(expert: np.ndarray, G: int):
     return ori, rowpos_flat.reshape(batch, topk), group_list
 
 
-def draw_values(rng: np.random.Generator, shape, dtype: str, std: float, integer: bool):
-    if integer:
-        v = rng.integers(-2, 3, size=shape).astype(np.float32)
-    else:
-        v = rng.standard_normal(size=shape, dtype=np.float32)
-        if std != 1.0:
-            v *= np.float32(std)
-    return to_storage(v, dtype)
+def draw_values(seed: int, tensor_id: int, shape, dtype: str, std: float, integer: bool):
+    """Values of one tensor, drawn in fixed blocks of 2^22 elements; block t
+    uses its own PCG64 stream seeded by (seed, tensor_id, t), so the result
+    does not depend on how many threads fill it."""
+    n = int(np.prod(shape))
+    v = np.empty(n, dtype=np.float32)
+
+    def work(t_se):
+        t, (s, e) = t_se
+        rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, tensor_id, t])))
+        if integer:
+            v[s:e] = rng.integers(-2, 3, size=e - s).astype(np.float32)
+        else:
+            rng.standard_normal(size=e - s, dtype=np.float32, out=v[s:e])
+            if std != 1.0:
+                v[s:e] *= np.float32(std)
+
+    with concurrent.futures.ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(work, enumerate(_blocks(n))))
+    return to_storage(v.reshape(shape), dtype)
 
 
 def make_case(batch: int, topk: int, G: int, K: int, N: int, dtype: str = "f32", *,
@@ -192,8 +240,8 @@ def make_case(batch: int, topk: int, G: int, K: int, N: int, dtype: str = "f32",
     expert = np.asarray(expert, dtype=np.int64)
     ori, rowpos, group_list = assemble(expert, G)
     M = batch * topk
-    grad_y = draw_values(rng, (M, N), dtype, y_std, integer)
-    weight = draw_values(rng, (G, K, N), dtype, w_std, integer)
+    grad_y = draw_values(seed, 1, (M, N), dtype, y_std, integer)
+    weight = draw_values(seed, 2, (G, K, N), dtype, w_std, integer)
     eri = ori.copy() if row_idx_type == 0 else rowpos.reshape(-1).copy()
     return Case(batch=batch, topk=topk, G=G, K=K, N=N, dtype=dtype,
                 row_idx_type=row_idx_type, grad_y=grad_y, weight=weight, eri=eri,

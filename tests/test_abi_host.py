@@ -1,0 +1,106 @@
+"""The C-ABI library on the host: it loads, exports every symbol the header
+declares, and its host-only paths (workspace query, plan, validation before
+any launch) behave as documented.  No kernel is launched here."""
+import ctypes
+
+import pytest
+
+import permute_grouped_gemm_amd as pgg
+
+pytestmark = pytest.mark.skipif(not __import__("os").path.exists(pgg.LIB_PATH),
+                                reason="libpgg.so not built")
+
+F32, F16, BF16 = 0, 1, 2
+
+
+def desc(M=128, N=64, G=4, K=96, L=None, Gl=None, batch=64, topk=2, rit=0, dy=F32, dw=None, Nw=None):
+    return pgg.make_desc((M, N), (G, K, N if Nw is None else Nw), M if L is None else L,
+                         G if Gl is None else Gl, batch, topk, rit, dy, dy if dw is None else dw)
+
+
+def status_of_size(d):
+    n = ctypes.c_size_t()
+    return pgg.lib().pgg_moe_dx_workspace_size(ctypes.byref(d), ctypes.byref(n)), n.value
+
+
+def test_library_exports_every_header_symbol():
+    names = pgg.header_functions()
+    assert "pgg_moe_dx" in names and "pgg_moe_dx_workspace_size" in names
+    L = pgg.lib()
+    missing = [n for n in names if not hasattr(L, n)]
+    assert not missing, missing
+    assert len(names) >= 10
+
+
+def test_status_strings():
+    for s in range(6):
+        assert pgg.lib().pgg_status_string(s)
+    assert pgg.lib().pgg_device_error_string(4) == b"expanded_row_idx is not a permutation"
+
+
+@pytest.mark.parametrize("bad", [
+    dict(Nw=65), dict(Gl=3), dict(L=127), dict(L=129), dict(M=130, L=130), dict(topk=0),
+    dict(batch=0), dict(rit=2), dict(dw=F16), dict(dy=3, dw=3), dict(G=0, Gl=0),
+])
+def test_invalid_descriptors_rejected(bad):
+    st, _ = status_of_size(desc(**bad))
+    assert st == pgg.ERR_INVALID_ARG
+
+
+def test_reserved_field_must_be_zero():
+    d = desc()
+    d.reserved = 1
+    assert status_of_size(d)[0] == pgg.ERR_INVALID_ARG
+
+
+def test_too_large_is_unsupported():
+    M = 1 << 31
+    st, _ = status_of_size(desc(M=M, batch=M // 2, topk=2))
+    assert st == pgg.ERR_UNSUPPORTED
+
+
+def test_ring_does_not_grow_with_M():
+    K, N, G = 7168, 2048, 60
+    plans = [pgg.plan_desc(desc(M=m, N=N, G=G, K=K, batch=m // 8, topk=8, dy=F16))
+             for m in (110592, 221184, 442368)]
+    assert len({p["ring_bytes"] for p in plans}) == 1
+    for p, m in zip(plans, (110592, 221184, 442368)):
+        assert p["ring_bytes"] <= 256 << 20
+        assert p["workspace_bytes"] < m * K * 4 // 8            # far below the [M,K] fp32 intermediate
+        assert p["workspace_bytes"] == p["table_bytes"] + p["ring_bytes"]
+        assert p["table_bytes"] % 512 == 0
+
+
+def test_plan_regimes():
+    assert pgg.plan_desc(desc(dy=F32))["regime"] == 2
+    decode = pgg.plan_desc(desc(M=128, N=4096, G=16, K=7168, batch=16, topk=8, dy=BF16))
+    assert decode["regime"] == 1 and decode["max_chunks"] == 1        # one chunk: pure slot order
+    large = pgg.plan_desc(desc(M=110592, N=2048, G=60, K=7168, batch=13824, topk=8, dy=F16))
+    assert large["regime"] == 0
+    assert large["max_tiles"] == -(-110592 // large["block_m"]) + 60
+    assert large["max_chunks"] * large["tiles_per_chunk"] >= large["max_tiles"]
+
+
+def test_execute_rejects_before_any_launch():
+    L = pgg.lib()
+    d = desc()
+    need = pgg.workspace_size_desc(d)
+    fake = 0x100000  # never dereferenced: every case below fails validation first
+    args = [fake, fake, fake, fake, fake]
+    # invalid descriptor
+    bad = desc(topk=0)
+    assert L.pgg_moe_dx(ctypes.byref(bad), *args, fake, need, None) == pgg.ERR_INVALID_ARG
+    # NULL pointers
+    assert L.pgg_moe_dx(ctypes.byref(d), None, fake, fake, fake, fake, fake, need, None) == pgg.ERR_INVALID_ARG
+    assert L.pgg_moe_dx(ctypes.byref(d), *args, None, need, None) == pgg.ERR_INVALID_ARG
+    # undersized workspace
+    assert L.pgg_moe_dx(ctypes.byref(d), *args, fake, need - 1, None) == pgg.ERR_WORKSPACE_TOO_SMALL
+    # misaligned workspace
+    assert L.pgg_moe_dx(ctypes.byref(d), *args, fake + 8, need, None) == pgg.ERR_MISALIGNED
+
+
+def test_timing_hook_guards():
+    L = pgg.lib()
+    assert L.pgg_timing_begin(0) == pgg.ERR_INVALID_ARG
+    n = ctypes.c_int32()
+    assert L.pgg_timing_end(None, 0, ctypes.byref(n)) == pgg.ERR_INVALID_ARG

@@ -1,0 +1,246 @@
+"""HIP path vs the CPU oracle, through the C-ABI library (needs an MI355X).
+
+Floating-point results are compared with the oracle's exact (double) d_x
+under the rules in parity.py; integer-valued inputs make every summation
+order exact, so there the HIP result must equal the oracle bit for bit; index
+tables must match exactly; repeated calls must be bit-identical.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import permute_grouped_gemm_amd as pgg
+import synth
+from gpu_util import bits, run, upload
+from parity import check_close
+
+pytestmark = pytest.mark.gpu
+
+
+def _exact(orc, case):
+    return orc.case_dx(case, mode=orc.EXACT, want_abs=True)
+
+
+def _parity(orc, case, got=None):
+    if got is None:
+        got = run(case)
+    exact, absdot = _exact(orc, case)
+    return check_close(got, exact, absdot, case.N, case.topk, case.dtype, case.name)
+
+
+# ---------------------------------------------------------------- small configs
+
+def test_tiny_f32(orc):
+    case = synth.make_config("tiny_f32")
+    _parity(orc, case)
+
+
+def test_tiny_f32_expert1_empty(orc):
+    case = synth.make_config("tiny_f32", empty=(1,), seed=7)
+    assert case.group_list[1] == 0
+    _parity(orc, case)
+
+
+@pytest.mark.parametrize("name,kw", synth.WHITEBOX, ids=[n for n, _ in synth.WHITEBOX])
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_whitebox(orc, name, kw, dtype):
+    kw = dict(kw)
+    kw.setdefault("row_idx_type", 0)
+    if name == "large_tokens" and dtype != "bf16":
+        pytest.skip("large-token case runs once, in bf16")
+    case = synth.make_case(dtype=dtype, seed=100, name=name, **kw)
+    _parity(orc, case)
+
+
+# ---------------------------------------------------------------- exact regime
+
+EXACT_SHAPES = [
+    dict(batch=64, topk=2, G=4, K=256, N=128),           # fp32 / several tiles
+    dict(batch=40, topk=8, G=16, K=7168, N=512, empty=(2, 5, 11)),   # weight-streaming tiles
+    dict(batch=600, topk=4, G=5, K=600, N=300),           # large tiles, row/col/reduction tails
+    dict(batch=10, topk=3, G=4, K=178, N=286),            # unaligned rows (N*2 % 16 != 0)
+]
+
+
+@pytest.mark.parametrize("kw", EXACT_SHAPES)
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_integer_inputs_bit_exact(orc, kw, dtype):
+    case = synth.make_case(dtype=dtype, seed=200, integer=True, **kw)
+    got = run(case)
+    want = orc.case_dx(case, mode=orc.SLOT)
+    np.testing.assert_array_equal(bits(got), bits(want))
+
+
+def test_many_chunks_bit_exact(orc, monkeypatch):
+    # a 1 MiB ring forces dozens of chunks: chunk-major order must still be exact
+    monkeypatch.setenv("PGG_RING_MB", "1")
+    case = synth.make_case(300, 4, 6, 1024, 256, "bf16", seed=201, integer=True)
+    gy, w, eri, gl = upload(case)
+    plan = pgg.plan(gy, w, eri, gl, case.batch, case.topk, 0)
+    assert plan["max_chunks"] >= 4, plan
+    got = run(case, tensors=(gy, w, eri, gl))
+    np.testing.assert_array_equal(bits(got), bits(orc.case_dx(case, mode=orc.SLOT)))
+
+
+def test_many_chunks_float(orc, monkeypatch):
+    monkeypatch.setenv("PGG_RING_MB", "2")
+    case = synth.make_case(900, 4, 12, 768, 512, "f16", seed=202, w_std=0.02, name="chunked")
+    _parity(orc, case)
+
+
+# ---------------------------------------------------------------- index tables
+
+@pytest.mark.parametrize("row_idx_type", [0, 1])
+@pytest.mark.parametrize("kw", [dict(batch=50, topk=3, G=7, K=64, N=64, empty=(4,)),
+                                dict(batch=3000, topk=8, G=16, K=64, N=64)])
+def test_index_tables_bit_exact(orc, row_idx_type, kw):
+    case = synth.make_case(dtype="bf16", seed=300, row_idx_type=row_idx_type, **kw)
+    gy, w, eri, gl = upload(case)
+    ws = torch.empty(pgg.workspace_size(gy, w, eri, gl, case.batch, case.topk, row_idx_type),
+                     dtype=torch.uint8, device="cuda")
+    run(case, tensors=(gy, w, eri, gl), workspace=ws)
+    inv, ori = pgg.debug_tables(gy, w, eri, gl, case.batch, case.topk, row_idx_type, ws)
+    o_ori, o_inv = orc.index(case.eri, row_idx_type)
+    np.testing.assert_array_equal(inv.numpy(), o_inv.astype(np.int32))
+    np.testing.assert_array_equal(ori.numpy(), o_ori.astype(np.int32))
+    tiles = pgg.debug_tiles(gy, w, eri, gl, case.batch, case.topk, row_idx_type, ws).numpy()
+    bm = pgg.plan(gy, w, eri, gl, case.batch, case.topk, row_idx_type)["block_m"]
+    off = orc.offsets(case.group_list, case.M)
+    want = [(g, off[g] + s, min(bm, case.group_list[g] - s))
+            for g in range(case.G) for s in range(0, int(case.group_list[g]), bm)]
+    np.testing.assert_array_equal(tiles, np.array(want, dtype=np.int32).reshape(-1, 3))
+
+
+# ---------------------------------------------------------------- invariants on the GPU
+
+def test_type0_and_type1_bitwise(orc):
+    a = synth.make_case(500, 8, 16, 512, 256, "bf16", seed=400, routing="zipf", row_idx_type=0)
+    b = synth.make_case(500, 8, 16, 512, 256, "bf16", seed=400, routing="zipf", row_idx_type=1)
+    ga, gb = run(a), run(b)
+    np.testing.assert_array_equal(bits(ga), bits(gb))
+    _parity(orc, a, ga)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_nan_in_empty_experts_never_read(orc, dtype):
+    case = synth.make_case(200, 4, 10, 384, 256, dtype, seed=401, empty=(0, 3, 9))
+    base = run(case)
+    W = case.weight.copy()
+    nan = synth.to_storage(np.full((case.K, case.N), np.nan, np.float32), dtype)
+    for g in (0, 3, 9):
+        W[g] = nan
+    case.weight = W
+    got = run(case)
+    assert not np.isnan(got).any()
+    np.testing.assert_array_equal(bits(got), bits(base))
+
+
+def test_row_shuffle_inside_groups_integer(orc):
+    case = synth.make_case(256, 4, 6, 320, 192, "f16", seed=402, integer=True)
+    rng = np.random.default_rng(3)
+    perm = np.arange(case.M)
+    start = 0
+    for cnt in case.group_list:
+        perm[start:start + cnt] = start + rng.permutation(cnt)
+        start += cnt
+    shuffled = synth.make_case(256, 4, 6, 320, 192, "f16", seed=402, integer=True)
+    shuffled.grad_y = case.grad_y[perm]
+    shuffled.eri = case.eri[perm]
+    np.testing.assert_array_equal(bits(run(shuffled)), bits(run(case)))
+
+
+@pytest.mark.parametrize("which", ["tiny", "stream", "large", "chunked"])
+def test_ten_runs_bit_identical(orc, which, monkeypatch):
+    if which == "tiny":
+        case = synth.make_config("tiny_f32")
+    elif which == "stream":
+        case = synth.make_case(16, 8, 16, 2048, 1024, "bf16", seed=500, empty=(1, 2, 3, 4))
+    elif which == "large":
+        case = synth.make_case(1024, 8, 8, 1024, 512, "f16", seed=501, w_std=0.02)
+    else:
+        monkeypatch.setenv("PGG_RING_MB", "2")
+        case = synth.make_case(1024, 8, 60, 512, 256, "f32", seed=502, routing="heavy",
+                               empty=tuple(range(0, 60, 5)), heavy=1, heavy_rows=2048)
+    tensors = upload(case)
+    first = run(case, tensors=tensors)
+    for _ in range(9):
+        np.testing.assert_array_equal(bits(run(case, tensors=tensors)), bits(first))
+
+
+# ---------------------------------------------------------------- device error word
+
+def _err(case):
+    gy, w, eri, gl = upload(case)
+    ws = torch.empty(pgg.workspace_size(gy, w, eri, gl, case.batch, case.topk, case.row_idx_type),
+                     dtype=torch.uint8, device="cuda")
+    pgg.moe_dx(gy, w, eri, gl, case.batch, case.topk, case.row_idx_type, workspace=ws)
+    return pgg.read_device_error(ws)
+
+
+@pytest.mark.parametrize("row_idx_type", [0, 1])
+def test_device_errors(row_idx_type):
+    base = dict(batch=32, topk=2, G=4, K=64, N=64, dtype="bf16", seed=600, row_idx_type=row_idx_type)
+    c = synth.make_case(**base)
+    c.group_list = c.group_list.copy()
+    c.group_list[1] -= 1
+    c.group_list[2] += 1
+    assert _err(c) == (pgg.DEV_OK, 0)          # still a valid split: no error
+    c.group_list[0] = -1
+    assert _err(c) == (pgg.DEV_GROUP_NEGATIVE, 0)
+    c = synth.make_case(**base)
+    c.group_list = c.group_list + np.array([0, 0, 0, 1])
+    assert _err(c) == (pgg.DEV_GROUP_SUM, c.M + 1)
+    c = synth.make_case(**base)
+    c.eri = c.eri.copy()
+    c.eri[5] = c.M
+    assert _err(c) == (pgg.DEV_INDEX_RANGE, 5)
+    c = synth.make_case(**base)
+    c.eri = c.eri.copy()
+    c.eri[7] = c.eri[3]
+    code, detail = _err(c)
+    assert code == pgg.DEV_INDEX_DUP and detail == min(c.eri[3], c.eri[7])
+    # a valid call on the same workspace afterwards clears the word
+    assert _err(synth.make_case(**base)) == (pgg.DEV_OK, 0)
+
+
+# ---------------------------------------------------------------- named workloads at full size
+
+def _sampled(orc, case, got, n=48, seed=0):
+    rng = np.random.default_rng(seed)
+    toks = np.unique(np.concatenate([[0, case.batch - 1], rng.choice(case.batch, n, replace=False)]))
+    d32, d64, ab = orc.case_dx_tokens(case, toks)
+    check_close(got[toks], d64, ab, case.N, case.topk, case.dtype, case.name + " sampled")
+    cols = np.unique(np.concatenate([[0, case.K - 1], rng.choice(case.K, 6, replace=False)]))
+    s, a = orc.case_colsum(case, cols)
+    colsum = got[:, cols].astype(np.float64).sum(0)
+    # the fp32 results of batch rows are summed in double; bound as for the elementwise check
+    tol = {"f32": 1e-5, "f16": 2e-3, "bf16": 2e-3}[case.dtype]
+    assert np.all(np.abs(colsum - s) <= tol * np.abs(s) + 8 * (case.N + case.topk) * 2.0 ** -24 * a), \
+        (colsum, s)
+
+
+def test_decode_bf16_full(orc):
+    case = synth.make_config("decode_bf16")
+    _parity(orc, case)
+
+
+def test_mid_bf16_sampled(orc):
+    case = synth.make_config("mid_bf16")
+    _sampled(orc, case, run(case))
+
+
+def test_large_f16_sampled(orc):
+    case = synth.make_config("large_f16")
+    _sampled(orc, case, run(case))
+
+
+@pytest.mark.parametrize("name", ["large_f32", "large_f32_tail"])
+def test_large_f32_sampled_and_deterministic(orc, name):
+    case = synth.make_config(name)
+    tensors = upload(case)
+    first = run(case, tensors=tensors)
+    _sampled(orc, case, first)
+    for _ in range(9):
+        np.testing.assert_array_equal(bits(run(case, tensors=tensors)), bits(first))

@@ -128,6 +128,21 @@ def test_column_sum_invariant(orc):
     np.testing.assert_allclose(dx.sum(axis=0), d64.sum(axis=0), rtol=1e-12, atol=1e-12)
 
 
+def test_colsum_matches_token_sums(orc):
+    # the sum over expanded rows equals the sum over tokens of d_x (Step 2 regroups rows)
+    c = synth.make_case(60, 4, 7, 20, 33, "bf16", seed=45, row_idx_type=1, empty=(3,))
+    exact, absdot = orc.case_dx(c, mode=orc.EXACT, want_abs=True)
+    cols = np.array([0, 7, 19, 7])
+    s, a = orc.case_colsum(c, cols)
+    np.testing.assert_allclose(s, exact.sum(0)[cols], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(a, absdot.sum(0)[cols], rtol=1e-12)
+    # and against a literal per-row evaluation in numpy
+    dy, W = _f64(c, c.grad_y), _f64(c, c.weight)
+    off = orc.offsets(c.group_list, c.M)
+    lit = sum(dy[i] @ W[np.searchsorted(off, i, side="right") - 1, 19] for i in range(c.M))
+    assert abs(s[2] - lit) <= 1e-12 * max(1.0, abs(lit))
+
+
 @pytest.mark.parametrize("s", [-3, 5])
 def test_power_of_two_scaling_is_bitwise(orc, s):
     c = synth.make_case(30, 2, 4, 9, 13, "f32", seed=32)
