@@ -16,30 +16,21 @@
 // columns).  Waves are laid out WM x WN over the tile; each wave owns a
 // (BM/WM) x (BN/WN) block of 32x32 MFMA accumulators.  The reduction runs in
 // stages of 8 chunks per row (64 elements for 16-bit types, 32 for fp32),
-// double-buffered in LDS with a register prefetch of the next stage.  LDS
-// rows are 128 bytes; chunk c of row r is stored at slot c ^ (r & 7) so the
-// 16-byte fragment reads of a wave spread over all banks.
+// double-buffered in LDS with a register prefetch of the next stage (SETS=1)
+// or of the next two stages (SETS=2, where registers allow).  LDS rows are
+// 128 bytes, with chunks XOR-swizzled (lds_slot) so fragment reads are free
+// of bank conflicts.
 //
 // Row tails (experts whose last tile is partial), column tails (K not a
 // multiple of BN) and reduction tails (N not a multiple of the stage) are
 // zero-filled on load and masked on store.  ALIGNED=false handles rows that
 // are not 16-byte aligned (N*elem_size % 16 != 0 or unaligned base pointers)
 // with element loads.
-#include "pgg_internal.h"
+#include "pgg_device.h"
 
 namespace pgg {
 
 namespace {
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-
-struct TBf16 { using elem = uint16_t; static constexpr int kPerChunk = 8; };
-struct TF16 { using elem = uint16_t; static constexpr int kPerChunk = 8; };
-struct TF32 { using elem = float; static constexpr int kPerChunk = 4; };
 
 constexpr int kChunks = 8;  // 16-byte chunks per LDS row (one stage of the reduction)
 
@@ -54,32 +45,13 @@ struct GemmArgs {
   int32_t chunk, tc, n_col_tiles;
 };
 
-// Accumulate one chunk pair: lane half h holds chunk 2q+h of its row for both
-// operands, so the MFMA's reduction slots pair equal reduction indices.
-template <class T>
-__device__ __forceinline__ void mma(f32x16_t& acc, u32x4_t a, u32x4_t b);
-
-template <>
-__device__ __forceinline__ void mma<TBf16>(f32x16_t& acc, u32x4_t a, u32x4_t b) {
-  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
-}
-
-template <>
-__device__ __forceinline__ void mma<TF16>(f32x16_t& acc, u32x4_t a, u32x4_t b) {
-  acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
-                                               __builtin_bit_cast(f16x8_t, b), acc, 0, 0, 0);
-}
-
-template <>
-__device__ __forceinline__ void mma<TF32>(f32x16_t& acc, u32x4_t a, u32x4_t b) {
-  const f32x4_t fa = __builtin_bit_cast(f32x4_t, a);
-  const f32x4_t fb = __builtin_bit_cast(f32x4_t, b);
-  acc = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[0], fb[0], acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[1], fb[1], acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[2], fb[2], acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[3], fb[3], acc, 0, 0, 0);
-}
+// Physical 16-byte slot of chunk c of LDS row r.  A wave's 128-bit LDS
+// reads are served 16 lanes at a time over 64 four-byte banks (256 bytes), and
+// a fragment read puts 16 consecutive rows, same logical chunk, in those 16
+// lanes.  Rows are 128 bytes, so row parity picks the bank half; XOR-ing the
+// chunk with (r >> 1) & 7 gives the 8 rows of each parity 8 different slots:
+// all 16 lanes hit different banks.
+__device__ __forceinline__ int lds_slot(int r, int c) { return c ^ ((r >> 1) & 7); }
 
 // Load one 16-byte chunk of a row (elements [n, n + kPerChunk)), zero outside
 // the row or past N.
@@ -101,8 +73,20 @@ __device__ __forceinline__ u32x4_t load_chunk(const typename T::elem* __restrict
   return v;
 }
 
-template <class T, int BM, int BN, int WM, int WN, bool ALIGNED>
-__global__ __launch_bounds__(WM * WN * 64) void produce_kernel(GemmArgs a) {
+// Waves per SIMD each tile is built for: the 256x256 tile holds 256
+// accumulator registers per lane (one wave per SIMD); the narrow
+// weight-streaming tile wants many waves in flight; the fp32 tile two.
+template <int BM, int BN>
+constexpr int waves_per_eu() { return BM * BN >= 256 * 256 ? 1 : (BM <= 32 ? 4 : 2); }
+
+// Tiles whose workgroups reuse each other's operands get the XCD raster.
+template <int BM>
+constexpr bool kRaster() { return BM > 32; }
+
+template <class T, int BM, int BN, int WM, int WN, int SETS, bool ALIGNED>
+__global__ __launch_bounds__(WM * WN * 64)
+__attribute__((amdgpu_waves_per_eu(waves_per_eu<BM, BN>(), waves_per_eu<BM, BN>())))
+void produce_kernel(GemmArgs a) {
   using E = typename T::elem;
   constexpr int NT = WM * WN * 64;
   constexpr int EPC = T::kPerChunk;
@@ -117,8 +101,16 @@ __global__ __launch_bounds__(WM * WN * 64) void produce_kernel(GemmArgs a) {
   __shared__ u32x4_t lds[2][A_CHUNKS + B_CHUNKS];
 
   if (a.hdr->err != kNoError) return;
-  const int slot = blockIdx.x / a.n_col_tiles;
-  const int ct = blockIdx.x - slot * a.n_col_tiles;
+  int slot, ct;
+  if constexpr (kRaster<BM>()) {
+    if (!raster<8, 4>(blockIdx.x, a.tc, a.n_col_tiles, slot, ct)) return;
+  } else {
+    // streaming tiles share nothing: column tile fastest keeps the active
+    // m-tiles (the first ones of the chunk) on consecutive ids, spread over
+    // all XCDs by the round-robin dispatch
+    slot = blockIdx.x / a.n_col_tiles;
+    ct = blockIdx.x - slot * a.n_col_tiles;
+  }
   const int64_t tile_idx = static_cast<int64_t>(a.chunk) * a.tc + slot;
   if (tile_idx >= a.hdr->n_tiles) return;
   const MTile tile = a.tiles[tile_idx];
@@ -141,9 +133,12 @@ __global__ __launch_bounds__(WM * WN * 64) void produce_kernel(GemmArgs a) {
   const int lr = lane & 31;
   const int lh = lane >> 5;
 
-  // Per-thread staging slots: chunk id q -> (row q / 8, chunk q % 8).
-  u32x4_t ra[A_PER_T], rb[B_PER_T];
-  auto load_stage = [&](int kt) {
+  // Per-thread staging slots: chunk id q -> (row q / 8, chunk q % 8).  Two
+  // register sets alternate, so the loads of stage kt+2 are issued while
+  // stage kt is multiplied and stage kt+1 waits in registers.
+  u32x4_t ra0[A_PER_T], rb0[B_PER_T];
+  u32x4_t ra1[SETS == 2 ? A_PER_T : 1], rb1[SETS == 2 ? B_PER_T : 1];
+  auto load_stage = [&](int kt, auto& ra, auto& rb) {
     const int64_t n0 = static_cast<int64_t>(kt) * BK;
 #pragma unroll
     for (int s = 0; s < A_PER_T; ++s) {
@@ -158,18 +153,18 @@ __global__ __launch_bounds__(WM * WN * 64) void produce_kernel(GemmArgs a) {
       rb[s] = load_chunk<T, ALIGNED>(Bb + static_cast<int64_t>(r) * N, r < cols, n0 + c * EPC, N);
     }
   };
-  auto store_stage = [&](int buf) {
+  auto store_stage = [&](int buf, const auto& ra, const auto& rb) {
 #pragma unroll
     for (int s = 0; s < A_PER_T; ++s) {
       const int q = tid + s * NT;
       const int r = q >> 3, c = q & 7;
-      lds[buf][r * kChunks + (c ^ (r & 7))] = ra[s];
+      lds[buf][r * kChunks + lds_slot(r, c)] = ra[s];
     }
 #pragma unroll
     for (int s = 0; s < B_PER_T; ++s) {
       const int q = tid + s * NT;
       const int r = q >> 3, c = q & 7;
-      lds[buf][A_CHUNKS + r * kChunks + (c ^ (r & 7))] = rb[s];
+      lds[buf][A_CHUNKS + r * kChunks + lds_slot(r, c)] = rb[s];
     }
   };
 
@@ -181,31 +176,66 @@ __global__ __launch_bounds__(WM * WN * 64) void produce_kernel(GemmArgs a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  const int nk = static_cast<int>((N + BK - 1) / BK);
-  load_stage(0);
-  store_stage(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) load_stage(kt + 1);
+  // One stage: kChunks/2 chunk pairs.  Fragments are double-buffered in
+  // registers so the LDS reads of pair q+1 are in flight while the MFMAs of
+  // pair q run.
+  auto compute = [&](int buf) {
     const u32x4_t* As = lds[buf];
     const u32x4_t* Bs = lds[buf] + A_CHUNKS;
+    u32x4_t fa[2][FM], fb[2][FN];
+    auto load_frags = [&](int q, u32x4_t (&xa)[FM], u32x4_t (&xb)[FN]) {
+      const int sw = lds_slot(lr, 2 * q + lh);   // fragment rows start at multiples of 32
+#pragma unroll
+      for (int i = 0; i < FM; ++i) xa[i] = As[(wm * WTM + i * 32 + lr) * kChunks + sw];
+#pragma unroll
+      for (int j = 0; j < FN; ++j) xb[j] = Bs[(wn * WTN + j * 32 + lr) * kChunks + sw];
+    };
+    load_frags(0, fa[0], fb[0]);
 #pragma unroll
     for (int q = 0; q < kChunks / 2; ++q) {
-      const int c = 2 * q + lh;
-      const int sw = c ^ (lr & 7);   // rows of a fragment start at multiples of 32
-      u32x4_t fa[FM], fb[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i) fa[i] = As[(wm * WTM + i * 32 + lr) * kChunks + sw];
-#pragma unroll
-      for (int j = 0; j < FN; ++j) fb[j] = Bs[(wn * WTN + j * 32 + lr) * kChunks + sw];
+      // Issue the next pair's LDS reads, then this pair's MFMAs; the
+      // scheduling fences keep the compiler from sinking each read down to
+      // its first use, which would stall the MFMA pipe on LDS latency.
+      if (q + 1 < kChunks / 2) load_frags(q + 1, fa[(q + 1) & 1], fb[(q + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) mma<T>(acc[i][j], fa[i], fb[j]);
+        for (int j = 0; j < FN; ++j) mma<T>(acc[i][j], fa[q & 1][i], fb[q & 1][j]);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (kt + 1 < nk) store_stage(buf ^ 1);
+  };
+
+  // LDS buffer b holds stage kt when kt % 2 == b.
+  const int nk = static_cast<int>((N + BK - 1) / BK);
+  load_stage(0, ra0, rb0);
+  store_stage(0, ra0, rb0);
+  if constexpr (SETS == 1) {
+    // one register set: stage kt+1 is loaded while stage kt is multiplied
     __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      const int buf = kt & 1;
+      if (kt + 1 < nk) load_stage(kt + 1, ra0, rb0);
+      compute(buf);
+      if (kt + 1 < nk) store_stage(buf ^ 1, ra0, rb0);
+      __syncthreads();
+    }
+  } else {
+    if (nk > 1) load_stage(1, ra1, rb1);
+    __syncthreads();
+    for (int kt = 0; kt < nk; kt += 2) {
+      // stage kt in LDS 0, stage kt+1 in flight in set 1
+      if (kt + 2 < nk) load_stage(kt + 2, ra0, rb0);
+      compute(0);
+      if (kt + 1 < nk) store_stage(1, ra1, rb1);
+      __syncthreads();
+      if (kt + 1 >= nk) break;
+      // stage kt+1 in LDS 1, stage kt+2 in flight in set 0
+      if (kt + 3 < nk) load_stage(kt + 3, ra1, rb1);
+      compute(1);
+      if (kt + 2 < nk) store_stage(0, ra0, rb0);
+      __syncthreads();
+    }
   }
 
   // Epilogue: accumulator v of lane (lr, lh) is row 8*(v/4) + 4*lh + v%4,
@@ -225,22 +255,24 @@ __global__ __launch_bounds__(WM * WN * 64) void produce_kernel(GemmArgs a) {
   }
 }
 
-template <class T, int BM, int BN, int WM, int WN>
+template <class T, int BM, int BN, int WM, int WN, int SETS>
 hipError_t launch_cfg(const Plan& p, const GemmArgs& args, bool aligned, hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>(p.tc) * static_cast<unsigned>(p.n_col_tiles));
+  unsigned tiles = static_cast<unsigned>(p.tc) * static_cast<unsigned>(p.n_col_tiles);
+  if (kRaster<BM>()) tiles = (tiles + 255u) / 256u * 256u;   // whole rounds of 8 super-blocks
+  const dim3 grid(tiles);
   const dim3 block(WM * WN * 64);
   if (aligned)
-    hipLaunchKernelGGL((produce_kernel<T, BM, BN, WM, WN, true>), grid, block, 0, s, args);
+    hipLaunchKernelGGL((produce_kernel<T, BM, BN, WM, WN, SETS, true>), grid, block, 0, s, args);
   else
-    hipLaunchKernelGGL((produce_kernel<T, BM, BN, WM, WN, false>), grid, block, 0, s, args);
+    hipLaunchKernelGGL((produce_kernel<T, BM, BN, WM, WN, SETS, false>), grid, block, 0, s, args);
   return hipGetLastError();
 }
 
 template <class T>
 hipError_t launch_typed(const Plan& p, const GemmArgs& args, bool aligned, hipStream_t s) {
   switch (p.regime) {
-    case kLarge: return launch_cfg<T, 256, 256, 2, 2>(p, args, aligned, s);
-    case kStream: return launch_cfg<T, 32, 128, 1, 4>(p, args, aligned, s);
+    case kLarge: return launch_cfg<T, 256, 256, 2, 2, 1>(p, args, aligned, s);
+    case kStream: return launch_cfg<T, 32, 128, 1, 4, 2>(p, args, aligned, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -257,6 +289,7 @@ const char* produce_kernel_name(const Plan& p) {
 
 hipError_t launch_produce(const Plan& p, int chunk, const void* grad_y, const void* weight,
                           bool aligned, const WsView& w, hipStream_t s) {
+  if (produce_uses_dma(p, aligned)) return launch_produce_dma(p, chunk, grad_y, weight, w, s);
   GemmArgs args;
   args.A = grad_y;
   args.B = weight;
@@ -272,7 +305,7 @@ hipError_t launch_produce(const Plan& p, int chunk, const void* grad_y, const vo
   switch (p.dtype) {
     case PGG_BF16: return launch_typed<TBf16>(p, args, aligned, s);
     case PGG_F16: return launch_typed<TF16>(p, args, aligned, s);
-    default: return launch_cfg<TF32, 128, 128, 2, 2>(p, args, aligned, s);
+    default: return launch_cfg<TF32, 128, 128, 2, 2, 1>(p, args, aligned, s);
   }
 }
 

@@ -25,7 +25,8 @@ struct alignas(16) WsHeader {
   unsigned long long err;
   int32_t n_tiles;      // m-tiles actually produced by the group pass
   int32_t reserved0;
-  int64_t reserved[6];
+  int64_t zero[2];      // 16 zero bytes: the source of masked-off direct-to-LDS loads
+  int64_t reserved[4];
 };
 
 // One m-tile: up to block_m consecutive expanded rows of one expert.
@@ -100,6 +101,9 @@ hipError_t launch_prep_index(const Plan& p, const int64_t* eri, const WsView& w,
 hipError_t launch_prep_verify(const Plan& p, const int64_t* eri, const WsView& w, hipStream_t s);
 
 // Producer: chunk c's m-tiles x all column tiles -> ring rows.
+bool produce_uses_dma(const Plan& p, bool aligned);
+hipError_t launch_produce_dma(const Plan& p, int chunk, const void* grad_y, const void* weight,
+                              const WsView& w, hipStream_t s);
 hipError_t launch_produce(const Plan& p, int chunk, const void* grad_y, const void* weight,
                           bool aligned, const WsView& w, hipStream_t s);
 

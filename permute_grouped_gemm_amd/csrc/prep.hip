@@ -44,6 +44,8 @@ __device__ void reset_header(WsHeader* h) {
   if (threadIdx.x == 0) {
     h->err = kNoError;
     h->n_tiles = 0;
+    h->zero[0] = 0;
+    h->zero[1] = 0;
   }
 }
 
