@@ -4,28 +4,30 @@
 // cube output, §2.6.2) on 256x256 output tiles, written into the chunk's ring
 // rows.
 //
-// Operand staging is direct global -> LDS (global_load_lds_dwordx4: each
-// lane's 16 bytes land at M0 + 16 * lane), so no registers or ds_write
-// instructions carry the tiles.  Four LDS stages of 32 reduction elements
-// (32 KiB each: 256 d_y rows + 256 weight rows of 64 bytes) are in flight; a
-// stage is consumed three stages after its loads were issued.  The loads are
-// issued by inline assembly so that the compiler does not serialise them with
-// a blanket wait before every LDS read; the waits on their counter are
-// explicit (vmcnt counts loads in issue order).
+// One workgroup per tile, mapped by the XCD super-block raster (raster<8,4>):
+// the 32 workgroups an XCD runs together share 8 d_y slabs and 4 weight slabs
+// in its L2.
 //
-// Per stage, per wave (2 x 2 waves, 128 x 128 accumulators each): two chunk
-// pairs of 16 MFMA 32x32x16.  The fragments of pair q+1 are read while pair q
-// multiplies, and the first pair of the next stage is read while the last
-// pair of this stage multiplies; one barrier per stage makes the next stage
-// visible and frees the buffer that is refilled.
+// Operand staging is direct global -> LDS (global_load_lds_dwordx4: lane i's
+// 16 bytes land at M0 + 16 i), two stages of 64 reduction elements (64 KiB
+// each: 256 d_y rows + 256 weight rows of 128 bytes, whole cache lines).  The
+// loads are issued by inline assembly so the compiler does not serialise them
+// with a blanket wait before every LDS read; the waits on their counter are
+// explicit (vector memory operations complete in issue order, and these loads
+// write no register).
 //
-// LDS rows are 64 bytes (4 chunks).  A wave's 128-bit reads are served 16
-// lanes at a time over 64 banks (256 bytes = 4 rows); fragment reads put 16
-// consecutive rows in those lanes, so chunk c of row r sits at slot
-// c ^ ((r >> 2) & 3): the 4 rows sharing a bank quarter get 4 different slots.
+// Per stage and wave (2 x 2 waves, 128 x 128 fp32 accumulators each): four
+// chunk pairs of 16 MFMA 32x32x16; the fragments of the next pair are read
+// while the current pair multiplies, across stage boundaries too.
 //
-// Masked-off lanes (rows past the tile's rows, columns past K, reduction
-// past N) load 16 zero bytes from the workspace header instead.
+// LDS rows are 128 bytes (8 chunks).  128-bit LDS reads are served 16 lanes
+// at a time over 64 banks (256 bytes = 2 rows); a fragment read puts 16
+// consecutive rows, same chunk, in those lanes, so chunk c of row r sits at
+// slot c ^ ((r >> 1) & 7): the 8 rows of each parity get 8 different slots.
+//
+// Masked-off lanes (rows past the tile's rows, columns past K, reduction past
+// N) load 16 zero bytes from the workspace header instead.  Ring stores are
+// non-temporal: the consumer reads them back from memory, not from this L2.
 #include "pgg_device.h"
 
 namespace pgg {
@@ -37,16 +39,24 @@ constexpr int kThreads = 256, kWaves = 4;
 constexpr int kWM = 2;                        // waves along rows
 constexpr int kWTM = 128, kWTN = 128;         // wave tile
 constexpr int kFM = kWTM / 32, kFN = kWTN / 32;
-constexpr int kRowChunks = 4;                 // 16-byte chunks per LDS row per stage
+constexpr int kRowChunks = 8;                 // 16-byte chunks per LDS row per stage
 constexpr int kBK = kRowChunks * 8;           // reduction elements per stage
-constexpr int kStages = 4;
+constexpr int kPairs = kRowChunks / 2;
+constexpr int kStages = 2;
 constexpr int kSlotsA = kBM * kRowChunks;
 constexpr int kSlotsB = kBN * kRowChunks;
 constexpr int kStageSlots = kSlotsA + kSlotsB;
-constexpr int kLoadsA = kSlotsA / kThreads;   // direct-to-LDS loads per thread per stage
+constexpr int kRowsPerLoad = 64 / kRowChunks;          // rows one wave instruction covers
+constexpr int kLoadsA = kSlotsA / kThreads;            // direct-to-LDS loads per thread per stage
 constexpr int kLoadsB = kSlotsB / kThreads;
 constexpr int kLoadsPerStage = kLoadsA + kLoadsB;
-static_assert(kLoadsPerStage * (kStages - 1) <= 63, "vmcnt range");
+constexpr int kSuperM = 8, kSuperN = 4;                // super-block of tiles per XCD round
+constexpr int kSuper = kSuperM * kSuperN;
+constexpr int kXcds = 8;
+static_assert(kLoadsPerStage * kStages <= 63, "vmcnt range");
+static_assert(kPairs % 2 == 0, "a stage must end on the second fragment set");
+static_assert(kRowsPerLoad * kWaves * kLoadsA == kBM && kRowsPerLoad * kWaves * kLoadsB == kBN,
+              "loads cover the tile rows");
 
 struct LargeArgs {
   const void* A;            // grad_y [M, N]
@@ -59,17 +69,17 @@ struct LargeArgs {
   int32_t chunk, tc, n_col_tiles;
 };
 
-__device__ __forceinline__ int slot_of(int r, int c) { return c ^ ((r >> 2) & 3); }
+__device__ __forceinline__ int slot_of(int r, int c) { return c ^ ((r >> 1) & 7); }
 
 __device__ __forceinline__ void dma16(const void* src, uint32_t m0) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
                :: "s"(m0), "v"(src) : "memory", "m0");
 }
 
-// Wait until at most `n` of this wave's direct-to-LDS loads are outstanding and
-// its LDS reads are done, then barrier the workgroup.  The wait is the
-// builtin (the compiler's wait insertion then knows the LDS reads are done);
-// the empty asm statements keep memory accesses from moving across.
+// Wait until at most N of this wave's vector memory operations are
+// outstanding and its LDS reads are done, then barrier the workgroup.  The
+// wait is the builtin (so the compiler knows the LDS reads are done); the
+// empty asm statements keep memory accesses from moving across.
 template <int N>
 __device__ __forceinline__ void wait_then_barrier() {
   // s_waitcnt immediate: vmcnt[3:0] in bits 3:0, expcnt 6:4 (7 = no wait),
@@ -81,15 +91,6 @@ __device__ __forceinline__ void wait_then_barrier() {
   asm volatile("" ::: "memory");
 }
 
-__device__ __forceinline__ void wait_stages_then_barrier(int stages_outstanding) {
-  switch (stages_outstanding) {
-    case 0: wait_then_barrier<0>(); break;
-    case 1: wait_then_barrier<kLoadsPerStage>(); break;
-    case 2: wait_then_barrier<2 * kLoadsPerStage>(); break;
-    default: wait_then_barrier<3 * kLoadsPerStage>(); break;
-  }
-}
-
 template <class T>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void produce_large_kernel(LargeArgs a) {
@@ -98,7 +99,7 @@ void produce_large_kernel(LargeArgs a) {
 
   if (a.hdr->err != kNoError) return;
   int slot, ct;
-  if (!raster<8, 4>(blockIdx.x, a.tc, a.n_col_tiles, slot, ct)) return;
+  if (!raster<kSuperM, kSuperN>(blockIdx.x, a.tc, a.n_col_tiles, slot, ct)) return;
   const int64_t tile_idx = static_cast<int64_t>(a.chunk) * a.tc + slot;
   if (tile_idx >= a.hdr->n_tiles) return;
   const MTile tile = a.tiles[tile_idx];
@@ -106,7 +107,6 @@ void produce_large_kernel(LargeArgs a) {
   const int rows = tile.rows;
   const int64_t col0 = static_cast<int64_t>(ct) * kBN;
   const int cols = static_cast<int>(min<int64_t>(kBN, a.K - col0));
-  const int64_t ring_row0 = static_cast<int64_t>(tile.row0) - a.chunk_row0[a.chunk];
   const int64_t N = a.N;
 
   const int tid = threadIdx.x;
@@ -114,30 +114,22 @@ void produce_large_kernel(LargeArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave % kWM, wn = wave / kWM;
   const int lr = lane & 31, lh = lane >> 5;
-
-  // Direct-to-LDS load j of this wave covers slots (j*4 + wave)*64 + lane of a
-  // region: row (j*4 + wave)*16 + lane/4, slot lane%4, whose logical chunk
-  // (lane%4) ^ ((lane/16)%4) is the same for every j.
-  const int dma_c = (lane & 3) ^ ((lane >> 4) & 3);
-  const E* pa[kLoadsA];
-  const E* pb[kLoadsB];
-  bool va[kLoadsA], vb[kLoadsB];
-  const E* Ab = static_cast<const E*>(a.A) + static_cast<int64_t>(tile.row0) * N + dma_c * 8;
-  const E* Bb = static_cast<const E*>(a.B) + (static_cast<int64_t>(tile.g) * a.K + col0) * N + dma_c * 8;
+  // Direct-to-LDS load j of this wave fills slots (j*4 + wave)*64 + lane of a
+  // region: row r0 + 32 j (r0 = wave*8 + lane/8), slot lane%8, which holds
+  // chunk (lane%8) ^ ((r0/2)%8) -- the same for every j.
+  const int r0 = wave * kRowsPerLoad + (lane >> 3);
+  const int dma_c = slot_of(r0, lane & 7);
+  const E* pa = static_cast<const E*>(a.A) + (static_cast<int64_t>(tile.row0) + r0) * N + dma_c * 8;
+  const E* pb =
+      static_cast<const E*>(a.B) + (static_cast<int64_t>(tile.g) * a.K + col0 + r0) * N + dma_c * 8;
+  uint32_t va = 0, vb = 0;   // bit j: load j's row lies inside the tile
 #pragma unroll
-  for (int j = 0; j < kLoadsA; ++j) {
-    const int r = (j * kWaves + wave) * 16 + (lane >> 2);
-    va[j] = r < rows;
-    pa[j] = Ab + static_cast<int64_t>(va[j] ? r : 0) * N;
-  }
+  for (int j = 0; j < kLoadsA; ++j) va |= (r0 + 32 * j < rows ? 1u : 0u) << j;
 #pragma unroll
-  for (int j = 0; j < kLoadsB; ++j) {
-    const int r = (j * kWaves + wave) * 16 + (lane >> 2);
-    vb[j] = r < cols;
-    pb[j] = Bb + static_cast<int64_t>(vb[j] ? r : 0) * N;
-  }
+  for (int j = 0; j < kLoadsB; ++j) vb |= (r0 + 32 * j < cols ? 1u : 0u) << j;
   const void* zero = a.hdr->zero;
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_offset(lds));
+  const int64_t row_step = 32 * N;
 
   auto issue = [&](int kt) {
     const uint32_t base = lds0 + static_cast<uint32_t>((kt % kStages) * kStageSlots * 16);
@@ -145,23 +137,15 @@ void produce_large_kernel(LargeArgs a) {
     const bool in_n = n0 + dma_c * 8 < N;
 #pragma unroll
     for (int j = 0; j < kLoadsA; ++j)
-      dma16(va[j] && in_n ? static_cast<const void*>(pa[j] + n0) : zero,
+      dma16(in_n && ((va >> j) & 1) ? static_cast<const void*>(pa + j * row_step + n0) : zero,
             base + static_cast<uint32_t>((j * kWaves + wave) * 64 * 16));
 #pragma unroll
     for (int j = 0; j < kLoadsB; ++j)
-      dma16(vb[j] && in_n ? static_cast<const void*>(pb[j] + n0) : zero,
+      dma16(in_n && ((vb >> j) & 1) ? static_cast<const void*>(pb + j * row_step + n0) : zero,
             base + static_cast<uint32_t>((kSlotsA + (j * kWaves + wave) * 64) * 16));
   };
 
-  f32x16_t acc[kFM][kFN];
-#pragma unroll
-  for (int i = 0; i < kFM; ++i)
-#pragma unroll
-    for (int j = 0; j < kFN; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-
-  // fragment rows start at multiples of 32, so (row >> 2) & 3 == (lr >> 2) & 3
+  // fragment rows start at multiples of 32, so (row >> 1) & 7 == (lr >> 1) & 7
   auto load_frags = [&](int kt, int q, u32x4_t (&fa)[kFM], u32x4_t (&fb)[kFN]) {
     const u32x4_t* st = lds + (kt % kStages) * kStageSlots;
     const int sl = slot_of(lr, 2 * q + lh);
@@ -170,6 +154,13 @@ void produce_large_kernel(LargeArgs a) {
 #pragma unroll
     for (int j = 0; j < kFN; ++j) fb[j] = st[kSlotsA + (wn * kWTN + j * 32 + lr) * kRowChunks + sl];
   };
+  f32x16_t acc[kFM][kFN];
+#pragma unroll
+  for (int i = 0; i < kFM; ++i)
+#pragma unroll
+    for (int j = 0; j < kFN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
   auto mfmas = [&](const u32x4_t (&fa)[kFM], const u32x4_t (&fb)[kFN]) {
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -183,47 +174,57 @@ void produce_large_kernel(LargeArgs a) {
 #pragma unroll
   for (int s = 0; s < kStages; ++s)
     if (s < nk) issue(s);
-  wait_stages_then_barrier(min(kStages, nk) - 1);
   u32x4_t fa0[kFM], fb0[kFN], fa1[kFM], fb1[kFN];
+  // stage 0 landed (stage 1, if any, may still be in flight)
+  if (nk > 1) wait_then_barrier<kLoadsPerStage>(); else wait_then_barrier<0>();
   load_frags(0, 0, fa0, fb0);
   int kt = 0;
-  // Steady state, free of branches so the compiler's LDS wait counts stay
-  // exact across iterations: stage kt+1 is complete after the barrier, and
-  // stages kt+2, kt+3 may still be landing.
+  // steady state, free of branches so the compiler's LDS wait counts stay exact
   for (; kt + kStages < nk; ++kt) {
-    load_frags(kt, 1, fa1, fb1);
-    mfmas(fa0, fb0);
-    wait_then_barrier<(kStages - 2) * kLoadsPerStage>();
-    issue(kt + kStages);            // refills stage kt's buffer
-    load_frags(kt + 1, 0, fa0, fb0);
-    mfmas(fa1, fb1);
-  }
-  // Drain: the last kStages stages, nothing left to issue.
-  for (; kt < nk; ++kt) {
-    load_frags(kt, 1, fa1, fb1);
-    mfmas(fa0, fb0);
-    if (kt + 1 < nk) {
-      wait_stages_then_barrier(nk - 2 - kt);
-      load_frags(kt + 1, 0, fa0, fb0);
+#pragma unroll
+    for (int q = 0; q < kPairs; ++q) {
+      if (q + 1 < kPairs) {
+        if (q & 1) load_frags(kt, q + 1, fa0, fb0); else load_frags(kt, q + 1, fa1, fb1);
+      } else {
+        // stage kt+1 landed everywhere and every wave is done with stage kt
+        wait_then_barrier<0>();
+        issue(kt + kStages);            // refills stage kt's buffer
+        load_frags(kt + 1, 0, fa0, fb0);
+      }
+      if (q & 1) mfmas(fa1, fb1); else mfmas(fa0, fb0);
     }
-    mfmas(fa1, fb1);
+  }
+  // last stages: nothing more to issue
+  for (; kt < nk; ++kt) {
+#pragma unroll
+    for (int q = 0; q < kPairs; ++q) {
+      if (q + 1 < kPairs) {
+        if (q & 1) load_frags(kt, q + 1, fa0, fb0); else load_frags(kt, q + 1, fa1, fb1);
+      } else if (kt + 1 < nk) {
+        wait_then_barrier<0>();
+        load_frags(kt + 1, 0, fa0, fb0);
+      }
+      if (q & 1) mfmas(fa1, fb1); else mfmas(fa0, fb0);
+    }
   }
 
   // Epilogue: accumulator v of lane (lr, lh) is row 8*(v/4) + 4*lh + v%4,
   // column lr of its 32x32 block.
+  const int64_t ring_row0 = static_cast<int64_t>(tile.row0) - a.chunk_row0[a.chunk];
   float* __restrict__ out = a.ring + ring_row0 * a.K + col0;
+  const bool full = rows == kBM && cols == kBN;
 #pragma unroll
-  for (int i = 0; i < kFM; ++i) {
+  for (int i = 0; i < kFM; ++i)
 #pragma unroll
     for (int j = 0; j < kFN; ++j) {
       const int n = wn * kWTN + j * 32 + lr;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int m = wm * kWTM + i * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
-        if (m < rows && n < cols) out[static_cast<int64_t>(m) * a.K + n] = acc[i][j][v];
+        if (full || (m < rows && n < cols))
+          __builtin_nontemporal_store(acc[i][j][v], out + static_cast<int64_t>(m) * a.K + n);
       }
     }
-  }
 }
 
 }  // namespace
@@ -247,7 +248,7 @@ hipError_t launch_produce_dma(const Plan& p, int chunk, const void* grad_y, cons
   a.tc = p.tc;
   a.n_col_tiles = p.n_col_tiles;
   unsigned tiles = static_cast<unsigned>(p.tc) * static_cast<unsigned>(p.n_col_tiles);
-  tiles = (tiles + 255u) / 256u * 256u;   // whole rounds of 8 super-blocks of 32 tiles
+  tiles = (tiles + kXcds * kSuper - 1) / (kXcds * kSuper) * (kXcds * kSuper);   // whole raster rounds
   if (p.dtype == PGG_BF16)
     hipLaunchKernelGGL(produce_large_kernel<TBf16>, dim3(tiles), dim3(kThreads), 0, s, a);
   else

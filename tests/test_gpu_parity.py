@@ -61,6 +61,7 @@ EXACT_SHAPES = [
     dict(batch=40, topk=8, G=16, K=7168, N=512, empty=(2, 5, 11)),   # weight-streaming tiles
     dict(batch=600, topk=4, G=5, K=600, N=300),           # large tiles, row/col/reduction tails
     dict(batch=10, topk=3, G=4, K=178, N=286),            # unaligned rows (N*2 % 16 != 0)
+    dict(batch=700, topk=4, G=5, K=1000, N=2040),         # large tiles, aligned rows, N % 64 != 0
 ]
 
 
