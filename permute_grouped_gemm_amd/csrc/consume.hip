@@ -14,7 +14,8 @@
 // either +0 (the token's first chunk) or the d_x row left by earlier chunks.
 // So each element's additions happen in an order fixed by the inputs and the
 // tile schedule alone, and repeated calls are bit-identical.  When the whole
-// problem is one chunk the order is exactly j = 0..topK-1.
+// problem is one chunk the order is exactly j = 0..topK-1, and the consumer is
+// indexed by token directly.
 #include "pgg_internal.h"
 
 namespace pgg {
@@ -90,6 +91,41 @@ __global__ __launch_bounds__(kConsumeThreads) void consume_kernel(ConsumeArgs a)
   }
 }
 
+// The whole problem is one chunk: every token's rows are all in the ring, so
+// token b simply adds its topK rows in slot order onto +0.  One workgroup per
+// (token, column block).
+template <int VEC>
+__global__ __launch_bounds__(kConsumeThreads) void consume_tokens_kernel(ConsumeArgs a) {
+  if (a.hdr->err != kNoError) return;
+  const int64_t b = blockIdx.x / a.col_blocks;
+  const int cb = static_cast<int>(blockIdx.x - b * a.col_blocks);
+  const int64_t k = (static_cast<int64_t>(cb) * kConsumeThreads + threadIdx.x) * VEC;
+  if (k >= a.K) return;
+  const int32_t* __restrict__ slots = a.inv + b * a.topk;
+  float acc[VEC];
+#pragma unroll
+  for (int v = 0; v < VEC; ++v) acc[v] = 0.0f;
+  for (int64_t j = 0; j < a.topk; ++j) {
+    const int64_t ij = slots[j];
+    if (ij < 0 || ij >= a.M) continue;
+    const float* __restrict__ src = a.ring + ij * a.K + k;
+    if constexpr (VEC == 4) {
+      const float4 s = *reinterpret_cast<const float4*>(src);
+      acc[0] += s.x; acc[1] += s.y; acc[2] += s.z; acc[3] += s.w;
+    } else {
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) acc[v] += src[v];
+    }
+  }
+  float* __restrict__ out = a.dx + b * a.K + k;
+  if constexpr (VEC == 4) {
+    *reinterpret_cast<float4*>(out) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  } else {
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) out[v] = acc[v];
+  }
+}
+
 }  // namespace
 
 hipError_t launch_consume(const Plan& p, int chunk, const WsView& w, float* grad_x, hipStream_t s) {
@@ -108,6 +144,15 @@ hipError_t launch_consume(const Plan& p, int chunk, const WsView& w, float* grad
   const int vec = vec4 ? 4 : 1;
   a.col_blocks = static_cast<int32_t>((p.K + int64_t(kConsumeThreads) * vec - 1) /
                                       (int64_t(kConsumeThreads) * vec));
+  if (p.max_chunks == 1) {
+    // one chunk holds every row: consume by token (chunk_row0[0] == 0 then)
+    const dim3 grid(static_cast<unsigned>(p.batch * a.col_blocks));
+    if (vec4)
+      hipLaunchKernelGGL(consume_tokens_kernel<4>, grid, dim3(kConsumeThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL(consume_tokens_kernel<1>, grid, dim3(kConsumeThreads), 0, s, a);
+    return hipGetLastError();
+  }
   const dim3 grid(static_cast<unsigned>(int64_t(p.ring_rows) * a.col_blocks));
   if (vec4)
     hipLaunchKernelGGL(consume_kernel<4>, grid, dim3(kConsumeThreads), 0, s, a);

@@ -32,7 +32,6 @@ namespace pgg {
 
 namespace {
 
-constexpr int kChunks = 8;  // 16-byte chunks per LDS row (one stage of the reduction)
 
 struct GemmArgs {
   const void* A;            // grad_y [M, N]
@@ -45,13 +44,17 @@ struct GemmArgs {
   int32_t chunk, tc, n_col_tiles;
 };
 
-// Physical 16-byte slot of chunk c of LDS row r.  A wave's 128-bit LDS
-// reads are served 16 lanes at a time over 64 four-byte banks (256 bytes), and
-// a fragment read puts 16 consecutive rows, same logical chunk, in those 16
-// lanes.  Rows are 128 bytes, so row parity picks the bank half; XOR-ing the
-// chunk with (r >> 1) & 7 gives the 8 rows of each parity 8 different slots:
-// all 16 lanes hit different banks.
-__device__ __forceinline__ int lds_slot(int r, int c) { return c ^ ((r >> 1) & 7); }
+// Physical 16-byte slot of chunk c of LDS row r (rows of CH chunks).  A
+// wave's 128-bit LDS reads are served 16 lanes at a time over 64 four-byte
+// banks (256 bytes), and a fragment read puts 16 consecutive rows, same
+// logical chunk, in those 16 lanes.  128-byte rows (CH 8): row parity picks
+// the bank half, and XOR-ing the chunk with (r >> 1) & 7 gives the 8 rows of
+// each parity 8 different slots.  256-byte rows (CH 16): XOR with r & 15 gives
+// the 16 rows 16 different slots.
+template <int CH>
+__device__ __forceinline__ int lds_slot(int r, int c) {
+  return CH == 16 ? (c ^ (r & 15)) : (c ^ ((r >> 1) & 7));
+}
 
 // Load one 16-byte chunk of a row (elements [n, n + kPerChunk)), zero outside
 // the row or past N.
@@ -83,13 +86,15 @@ constexpr int waves_per_eu() { return BM * BN >= 256 * 256 ? 1 : (BM <= 32 ? 4 :
 template <int BM>
 constexpr bool kRaster() { return BM > 32; }
 
-template <class T, int BM, int BN, int WM, int WN, int SETS, bool ALIGNED>
+template <class T, int BM, int BN, int WM, int WN, int SETS, int CH, bool ALIGNED>
 __global__ __launch_bounds__(WM * WN * 64)
 __attribute__((amdgpu_waves_per_eu(waves_per_eu<BM, BN>(), waves_per_eu<BM, BN>())))
 void produce_kernel(GemmArgs a) {
   using E = typename T::elem;
   constexpr int NT = WM * WN * 64;
   constexpr int EPC = T::kPerChunk;
+  constexpr int kChunks = CH;   // 16-byte chunks per LDS row (one stage of the reduction)
+  static_assert(CH == 8 || CH == 16, "row width");
   constexpr int BK = kChunks * EPC;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
@@ -143,13 +148,13 @@ void produce_kernel(GemmArgs a) {
 #pragma unroll
     for (int s = 0; s < A_PER_T; ++s) {
       const int q = tid + s * NT;
-      const int r = q >> 3, c = q & 7;
+      const int r = q / kChunks, c = q % kChunks;
       ra[s] = load_chunk<T, ALIGNED>(Ab + static_cast<int64_t>(r) * N, r < rows, n0 + c * EPC, N);
     }
 #pragma unroll
     for (int s = 0; s < B_PER_T; ++s) {
       const int q = tid + s * NT;
-      const int r = q >> 3, c = q & 7;
+      const int r = q / kChunks, c = q % kChunks;
       rb[s] = load_chunk<T, ALIGNED>(Bb + static_cast<int64_t>(r) * N, r < cols, n0 + c * EPC, N);
     }
   };
@@ -157,14 +162,14 @@ void produce_kernel(GemmArgs a) {
 #pragma unroll
     for (int s = 0; s < A_PER_T; ++s) {
       const int q = tid + s * NT;
-      const int r = q >> 3, c = q & 7;
-      lds[buf][r * kChunks + lds_slot(r, c)] = ra[s];
+      const int r = q / kChunks, c = q % kChunks;
+      lds[buf][r * kChunks + lds_slot<CH>(r, c)] = ra[s];
     }
 #pragma unroll
     for (int s = 0; s < B_PER_T; ++s) {
       const int q = tid + s * NT;
-      const int r = q >> 3, c = q & 7;
-      lds[buf][A_CHUNKS + r * kChunks + lds_slot(r, c)] = rb[s];
+      const int r = q / kChunks, c = q % kChunks;
+      lds[buf][A_CHUNKS + r * kChunks + lds_slot<CH>(r, c)] = rb[s];
     }
   };
 
@@ -184,7 +189,7 @@ void produce_kernel(GemmArgs a) {
     const u32x4_t* Bs = lds[buf] + A_CHUNKS;
     u32x4_t fa[2][FM], fb[2][FN];
     auto load_frags = [&](int q, u32x4_t (&xa)[FM], u32x4_t (&xb)[FN]) {
-      const int sw = lds_slot(lr, 2 * q + lh);   // fragment rows start at multiples of 32
+      const int sw = lds_slot<CH>(lr, 2 * q + lh);   // fragment rows start at multiples of 32
 #pragma unroll
       for (int i = 0; i < FM; ++i) xa[i] = As[(wm * WTM + i * 32 + lr) * kChunks + sw];
 #pragma unroll
@@ -255,24 +260,24 @@ void produce_kernel(GemmArgs a) {
   }
 }
 
-template <class T, int BM, int BN, int WM, int WN, int SETS>
+template <class T, int BM, int BN, int WM, int WN, int SETS, int CH>
 hipError_t launch_cfg(const Plan& p, const GemmArgs& args, bool aligned, hipStream_t s) {
   unsigned tiles = static_cast<unsigned>(p.tc) * static_cast<unsigned>(p.n_col_tiles);
   if (kRaster<BM>()) tiles = (tiles + 255u) / 256u * 256u;   // whole rounds of 8 super-blocks
   const dim3 grid(tiles);
   const dim3 block(WM * WN * 64);
   if (aligned)
-    hipLaunchKernelGGL((produce_kernel<T, BM, BN, WM, WN, SETS, true>), grid, block, 0, s, args);
+    hipLaunchKernelGGL((produce_kernel<T, BM, BN, WM, WN, SETS, CH, true>), grid, block, 0, s, args);
   else
-    hipLaunchKernelGGL((produce_kernel<T, BM, BN, WM, WN, SETS, false>), grid, block, 0, s, args);
+    hipLaunchKernelGGL((produce_kernel<T, BM, BN, WM, WN, SETS, CH, false>), grid, block, 0, s, args);
   return hipGetLastError();
 }
 
 template <class T>
 hipError_t launch_typed(const Plan& p, const GemmArgs& args, bool aligned, hipStream_t s) {
   switch (p.regime) {
-    case kLarge: return launch_cfg<T, 256, 256, 2, 2, 1>(p, args, aligned, s);
-    case kStream: return launch_cfg<T, 32, 128, 1, 4, 2>(p, args, aligned, s);
+    case kLarge: return launch_cfg<T, 256, 256, 2, 2, 1, 8>(p, args, aligned, s);
+    case kStream: return launch_cfg<T, 32, 64, 1, 2, 2, 8>(p, args, aligned, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -305,7 +310,7 @@ hipError_t launch_produce(const Plan& p, int chunk, const void* grad_y, const vo
   switch (p.dtype) {
     case PGG_BF16: return launch_typed<TBf16>(p, args, aligned, s);
     case PGG_F16: return launch_typed<TF16>(p, args, aligned, s);
-    default: return launch_cfg<TF32, 128, 128, 2, 2, 1>(p, args, aligned, s);
+    default: return launch_cfg<TF32, 128, 128, 2, 2, 1, 8>(p, args, aligned, s);
   }
 }
 

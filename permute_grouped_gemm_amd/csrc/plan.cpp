@@ -34,7 +34,7 @@ struct TileShape { int bm, bn; };
 TileShape tile_shape(int32_t regime) {
   switch (regime) {
     case kLarge: return {256, 256};
-    case kStream: return {32, 128};
+    case kStream: return {32, 64};
     default: return {128, 128};
   }
 }

@@ -197,7 +197,9 @@ PrepArgs prep_args(const Plan& p) {
 
 hipError_t launch_prep_fused(const Plan& p, const int64_t* eri, const int64_t* gl,
                              const WsView& w, hipStream_t s) {
-  hipLaunchKernelGGL(prep_fused_kernel, dim3(1), dim3(kPrepThreads), 0, s, prep_args(p), eri, gl, w);
+  // one wave for small problems: its scan barriers cost next to nothing
+  const unsigned threads = (p.M <= 4096 && p.G <= 4096) ? 64u : unsigned(kPrepThreads);
+  hipLaunchKernelGGL(prep_fused_kernel, dim3(1), dim3(threads), 0, s, prep_args(p), eri, gl, w);
   return hipGetLastError();
 }
 
