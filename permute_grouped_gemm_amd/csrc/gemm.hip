@@ -4,7 +4,10 @@
 //
 // (MoeInitRoutingGroupedMatmulGrad design page, §数学定义和公式 Step 1; the
 // page's cube output type is fp32 whatever the input type, §2.6.2), for the
-// m-tiles of one chunk, written into that chunk's fp32 ring rows.
+// m-tiles of one chunk, written into that chunk's fp32 ring rows.  This file
+// holds the general register-staged tile (fp32 inputs, and 16-bit inputs whose
+// rows are not 16-byte aligned); aligned 16-bit inputs take the direct-to-LDS
+// 256x256 tile or, with few rows per expert, the weight sweep.
 //
 // Both operands are contiguous along the reduction index n: a d_y row and a
 // W[g] row (one output column) are each a run of N elements.  That is the
@@ -16,10 +19,9 @@
 // columns).  Waves are laid out WM x WN over the tile; each wave owns a
 // (BM/WM) x (BN/WN) block of 32x32 MFMA accumulators.  The reduction runs in
 // stages of 8 chunks per row (64 elements for 16-bit types, 32 for fp32),
-// double-buffered in LDS with a register prefetch of the next stage (SETS=1)
-// or of the next two stages (SETS=2, where registers allow).  LDS rows are
-// 128 bytes, with chunks XOR-swizzled (lds_slot) so fragment reads are free
-// of bank conflicts.
+// double-buffered in LDS with a register prefetch of the next stage.  LDS
+// rows are 128 bytes, with chunks XOR-swizzled (lds_slot) so fragment reads
+// are free of bank conflicts.
 //
 // Row tails (experts whose last tile is partial), column tails (K not a
 // multiple of BN) and reduction tails (N not a multiple of the stage) are
@@ -44,57 +46,27 @@ struct GemmArgs {
   int32_t chunk, tc, n_col_tiles;
 };
 
-// Physical 16-byte slot of chunk c of LDS row r (rows of CH chunks).  A
+// Physical 16-byte slot of chunk c of LDS row r (rows of 8 chunks).  A
 // wave's 128-bit LDS reads are served 16 lanes at a time over 64 four-byte
 // banks (256 bytes), and a fragment read puts 16 consecutive rows, same
-// logical chunk, in those 16 lanes.  128-byte rows (CH 8): row parity picks
-// the bank half, and XOR-ing the chunk with (r >> 1) & 7 gives the 8 rows of
-// each parity 8 different slots.  256-byte rows (CH 16): XOR with r & 15 gives
-// the 16 rows 16 different slots.
-template <int CH>
-__device__ __forceinline__ int lds_slot(int r, int c) {
-  return CH == 16 ? (c ^ (r & 15)) : (c ^ ((r >> 1) & 7));
-}
-
-// Load one 16-byte chunk of a row (elements [n, n + kPerChunk)), zero outside
-// the row or past N.
-template <class T, bool ALIGNED>
-__device__ __forceinline__ u32x4_t load_chunk(const typename T::elem* __restrict__ row, bool row_ok,
-                                              int64_t n, int64_t N) {
-  using E = typename T::elem;
-  constexpr int EPC = T::kPerChunk;
-  u32x4_t v = {0u, 0u, 0u, 0u};
-  if (!row_ok || n >= N) return v;
-  if constexpr (ALIGNED) {
-    v = *reinterpret_cast<const u32x4_t*>(row + n);
-  } else {
-    E e[EPC];
-#pragma unroll
-    for (int t = 0; t < EPC; ++t) e[t] = (n + t < N) ? row[n + t] : E(0);
-    __builtin_memcpy(&v, e, sizeof(v));
-  }
-  return v;
-}
+// logical chunk, in those 16 lanes.  Row parity picks the bank half, and
+// XOR-ing the chunk with (r >> 1) & 7 gives the 8 rows of each parity 8
+// different slots.
+__device__ __forceinline__ int lds_slot(int r, int c) { return c ^ ((r >> 1) & 7); }
 
 // Waves per SIMD each tile is built for: the 256x256 tile holds 256
-// accumulator registers per lane (one wave per SIMD); the narrow
-// weight-streaming tile wants many waves in flight; the fp32 tile two.
+// accumulator registers per lane (one wave per SIMD); the fp32 tile two.
 template <int BM, int BN>
-constexpr int waves_per_eu() { return BM * BN >= 256 * 256 ? 1 : (BM <= 32 ? 4 : 2); }
+constexpr int waves_per_eu() { return BM * BN >= 256 * 256 ? 1 : 2; }
 
-// Tiles whose workgroups reuse each other's operands get the XCD raster.
-template <int BM>
-constexpr bool kRaster() { return BM > 32; }
-
-template <class T, int BM, int BN, int WM, int WN, int SETS, int CH, bool ALIGNED>
+template <class T, int BM, int BN, int WM, int WN, bool ALIGNED>
 __global__ __launch_bounds__(WM * WN * 64)
 __attribute__((amdgpu_waves_per_eu(waves_per_eu<BM, BN>(), waves_per_eu<BM, BN>())))
 void produce_kernel(GemmArgs a) {
   using E = typename T::elem;
   constexpr int NT = WM * WN * 64;
   constexpr int EPC = T::kPerChunk;
-  constexpr int kChunks = CH;   // 16-byte chunks per LDS row (one stage of the reduction)
-  static_assert(CH == 8 || CH == 16, "row width");
+  constexpr int kChunks = 8;    // 16-byte chunks per LDS row (one stage of the reduction)
   constexpr int BK = kChunks * EPC;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
@@ -107,15 +79,7 @@ void produce_kernel(GemmArgs a) {
 
   if (a.hdr->err != kNoError) return;
   int slot, ct;
-  if constexpr (kRaster<BM>()) {
-    if (!raster<8, 4>(blockIdx.x, a.tc, a.n_col_tiles, slot, ct)) return;
-  } else {
-    // streaming tiles share nothing: column tile fastest keeps the active
-    // m-tiles (the first ones of the chunk) on consecutive ids, spread over
-    // all XCDs by the round-robin dispatch
-    slot = blockIdx.x / a.n_col_tiles;
-    ct = blockIdx.x - slot * a.n_col_tiles;
-  }
+  if (!raster<8, 4>(blockIdx.x, a.tc, a.n_col_tiles, slot, ct)) return;
   const int64_t tile_idx = static_cast<int64_t>(a.chunk) * a.tc + slot;
   if (tile_idx >= a.hdr->n_tiles) return;
   const MTile tile = a.tiles[tile_idx];
@@ -138,11 +102,8 @@ void produce_kernel(GemmArgs a) {
   const int lr = lane & 31;
   const int lh = lane >> 5;
 
-  // Per-thread staging slots: chunk id q -> (row q / 8, chunk q % 8).  Two
-  // register sets alternate, so the loads of stage kt+2 are issued while
-  // stage kt is multiplied and stage kt+1 waits in registers.
+  // Per-thread staging slots: chunk id q -> (row q / 8, chunk q % 8).
   u32x4_t ra0[A_PER_T], rb0[B_PER_T];
-  u32x4_t ra1[SETS == 2 ? A_PER_T : 1], rb1[SETS == 2 ? B_PER_T : 1];
   auto load_stage = [&](int kt, auto& ra, auto& rb) {
     const int64_t n0 = static_cast<int64_t>(kt) * BK;
 #pragma unroll
@@ -163,13 +124,13 @@ void produce_kernel(GemmArgs a) {
     for (int s = 0; s < A_PER_T; ++s) {
       const int q = tid + s * NT;
       const int r = q / kChunks, c = q % kChunks;
-      lds[buf][r * kChunks + lds_slot<CH>(r, c)] = ra[s];
+      lds[buf][r * kChunks + lds_slot(r, c)] = ra[s];
     }
 #pragma unroll
     for (int s = 0; s < B_PER_T; ++s) {
       const int q = tid + s * NT;
       const int r = q / kChunks, c = q % kChunks;
-      lds[buf][A_CHUNKS + r * kChunks + lds_slot<CH>(r, c)] = rb[s];
+      lds[buf][A_CHUNKS + r * kChunks + lds_slot(r, c)] = rb[s];
     }
   };
 
@@ -189,7 +150,7 @@ void produce_kernel(GemmArgs a) {
     const u32x4_t* Bs = lds[buf] + A_CHUNKS;
     u32x4_t fa[2][FM], fb[2][FN];
     auto load_frags = [&](int q, u32x4_t (&xa)[FM], u32x4_t (&xb)[FN]) {
-      const int sw = lds_slot<CH>(lr, 2 * q + lh);   // fragment rows start at multiples of 32
+      const int sw = lds_slot(lr, 2 * q + lh);   // fragment rows start at multiples of 32
 #pragma unroll
       for (int i = 0; i < FM; ++i) xa[i] = As[(wm * WTM + i * 32 + lr) * kChunks + sw];
 #pragma unroll
@@ -215,32 +176,14 @@ void produce_kernel(GemmArgs a) {
   const int nk = static_cast<int>((N + BK - 1) / BK);
   load_stage(0, ra0, rb0);
   store_stage(0, ra0, rb0);
-  if constexpr (SETS == 1) {
-    // one register set: stage kt+1 is loaded while stage kt is multiplied
+  // stage kt+1 is loaded into registers while stage kt is multiplied
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) load_stage(kt + 1, ra0, rb0);
+    compute(buf);
+    if (kt + 1 < nk) store_stage(buf ^ 1, ra0, rb0);
     __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      const int buf = kt & 1;
-      if (kt + 1 < nk) load_stage(kt + 1, ra0, rb0);
-      compute(buf);
-      if (kt + 1 < nk) store_stage(buf ^ 1, ra0, rb0);
-      __syncthreads();
-    }
-  } else {
-    if (nk > 1) load_stage(1, ra1, rb1);
-    __syncthreads();
-    for (int kt = 0; kt < nk; kt += 2) {
-      // stage kt in LDS 0, stage kt+1 in flight in set 1
-      if (kt + 2 < nk) load_stage(kt + 2, ra0, rb0);
-      compute(0);
-      if (kt + 1 < nk) store_stage(1, ra1, rb1);
-      __syncthreads();
-      if (kt + 1 >= nk) break;
-      // stage kt+1 in LDS 1, stage kt+2 in flight in set 0
-      if (kt + 3 < nk) load_stage(kt + 3, ra1, rb1);
-      compute(1);
-      if (kt + 2 < nk) store_stage(0, ra0, rb0);
-      __syncthreads();
-    }
   }
 
   // Epilogue: accumulator v of lane (lr, lh) is row 8*(v/4) + 4*lh + v%4,
@@ -260,24 +203,23 @@ void produce_kernel(GemmArgs a) {
   }
 }
 
-template <class T, int BM, int BN, int WM, int WN, int SETS, int CH>
+template <class T, int BM, int BN, int WM, int WN>
 hipError_t launch_cfg(const Plan& p, const GemmArgs& args, bool aligned, hipStream_t s) {
   unsigned tiles = static_cast<unsigned>(p.tc) * static_cast<unsigned>(p.n_col_tiles);
-  if (kRaster<BM>()) tiles = (tiles + 255u) / 256u * 256u;   // whole rounds of 8 super-blocks
+  tiles = (tiles + 255u) / 256u * 256u;   // whole rounds of 8 super-blocks
   const dim3 grid(tiles);
   const dim3 block(WM * WN * 64);
   if (aligned)
-    hipLaunchKernelGGL((produce_kernel<T, BM, BN, WM, WN, SETS, CH, true>), grid, block, 0, s, args);
+    hipLaunchKernelGGL((produce_kernel<T, BM, BN, WM, WN, true>), grid, block, 0, s, args);
   else
-    hipLaunchKernelGGL((produce_kernel<T, BM, BN, WM, WN, SETS, CH, false>), grid, block, 0, s, args);
+    hipLaunchKernelGGL((produce_kernel<T, BM, BN, WM, WN, false>), grid, block, 0, s, args);
   return hipGetLastError();
 }
 
 template <class T>
 hipError_t launch_typed(const Plan& p, const GemmArgs& args, bool aligned, hipStream_t s) {
   switch (p.regime) {
-    case kLarge: return launch_cfg<T, 256, 256, 2, 2, 1, 8>(p, args, aligned, s);
-    case kStream: return launch_cfg<T, 32, 64, 1, 2, 2, 8>(p, args, aligned, s);
+    case kLarge: return launch_cfg<T, 256, 256, 2, 2>(p, args, aligned, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -294,6 +236,7 @@ const char* produce_kernel_name(const Plan& p) {
 
 hipError_t launch_produce(const Plan& p, int chunk, const void* grad_y, const void* weight,
                           bool aligned, const WsView& w, hipStream_t s) {
+  if (p.regime == kStream) return launch_produce_sweep(p, chunk, grad_y, weight, aligned, w, s);
   if (produce_uses_dma(p, aligned)) return launch_produce_dma(p, chunk, grad_y, weight, w, s);
   GemmArgs args;
   args.A = grad_y;
@@ -310,7 +253,7 @@ hipError_t launch_produce(const Plan& p, int chunk, const void* grad_y, const vo
   switch (p.dtype) {
     case PGG_BF16: return launch_typed<TBf16>(p, args, aligned, s);
     case PGG_F16: return launch_typed<TF16>(p, args, aligned, s);
-    default: return launch_cfg<TF32, 128, 128, 2, 2, 1, 8>(p, args, aligned, s);
+    default: return launch_cfg<TF32, 128, 128, 2, 2>(p, args, aligned, s);
   }
 }
 

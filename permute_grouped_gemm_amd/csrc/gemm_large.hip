@@ -71,26 +71,6 @@ struct LargeArgs {
 
 __device__ __forceinline__ int slot_of(int r, int c) { return c ^ ((r >> 1) & 7); }
 
-__device__ __forceinline__ void dma16(const void* src, uint32_t m0) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
-               :: "s"(m0), "v"(src) : "memory", "m0");
-}
-
-// Wait until at most N of this wave's vector memory operations are
-// outstanding and its LDS reads are done, then barrier the workgroup.  The
-// wait is the builtin (so the compiler knows the LDS reads are done); the
-// empty asm statements keep memory accesses from moving across.
-template <int N>
-__device__ __forceinline__ void wait_then_barrier() {
-  // s_waitcnt immediate: vmcnt[3:0] in bits 3:0, expcnt 6:4 (7 = no wait),
-  // lgkmcnt 11:8 (0), vmcnt[5:4] in bits 15:14
-  constexpr int kImm = (N & 15) | (7 << 4) | ((N >> 4) << 14);
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(kImm);
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 template <class T>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void produce_large_kernel(LargeArgs a) {

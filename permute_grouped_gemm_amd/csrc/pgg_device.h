@@ -16,6 +16,26 @@ struct TF16 { using elem = uint16_t; static constexpr int kPerChunk = 8; };
 struct TF32 { using elem = float; static constexpr int kPerChunk = 4; };
 
 
+// Load one 16-byte chunk of a row (elements [n, n + kPerChunk)), zero outside
+// the row or past N.
+template <class T, bool ALIGNED>
+__device__ __forceinline__ u32x4_t load_chunk(const typename T::elem* __restrict__ row, bool row_ok,
+                                              int64_t n, int64_t N) {
+  using E = typename T::elem;
+  constexpr int EPC = T::kPerChunk;
+  u32x4_t v = {0u, 0u, 0u, 0u};
+  if (!row_ok || n >= N) return v;
+  if constexpr (ALIGNED) {
+    v = *reinterpret_cast<const u32x4_t*>(row + n);
+  } else {
+    E e[EPC];
+#pragma unroll
+    for (int t = 0; t < EPC; ++t) e[t] = (n + t < N) ? row[n + t] : E(0);
+    __builtin_memcpy(&v, e, sizeof(v));
+  }
+  return v;
+}
+
 // Accumulate one chunk pair: lane half h holds chunk 2q+h of its row for both
 // operands, so the MFMA's reduction slots pair equal reduction indices.
 template <class T>
@@ -73,6 +93,42 @@ __device__ __forceinline__ bool raster(int bid, int n_slots, int n_ct, int& slot
 __device__ __forceinline__ uint32_t lds_offset(const void* p) {
   return static_cast<uint32_t>(
       reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)p));
+}
+
+// Direct global -> LDS load of 16 bytes per lane: lane i's bytes land at LDS
+// byte offset m0 + 16 i.  Issued by inline assembly, so the compiler neither
+// tracks nor waits for it: the waits on the vector-memory counter are explicit
+// (vector memory operations complete in issue order, and these loads write no
+// register).
+__device__ __forceinline__ void dma16(const void* src, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(m0), "v"(src) : "memory", "m0");
+}
+
+// Wait until at most N of this wave's vector memory operations are
+// outstanding and its LDS reads are done, then barrier the workgroup.  The
+// wait is the builtin (so the compiler knows the LDS reads are done); the
+// empty asm statements keep memory accesses from moving across.
+template <int N>
+__device__ __forceinline__ void wait_then_barrier() {
+  // s_waitcnt immediate: vmcnt[3:0] in bits 3:0, expcnt 6:4 (7 = no wait),
+  // lgkmcnt 11:8 (0), vmcnt[5:4] in bits 15:14
+  constexpr int kImm = (N & 15) | (7 << 4) | ((N >> 4) << 14);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(kImm);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+
+// Wait for this wave's LDS operations only, then barrier the workgroup (for
+// data exchanged through LDS while direct-to-LDS loads stay in flight).
+__device__ __forceinline__ void lds_barrier() {
+  constexpr int kImm = 15 | (7 << 4) | (3 << 14);   // vmcnt 63 (no wait), expcnt 7, lgkmcnt 0
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(kImm);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 }  // namespace pgg

@@ -102,6 +102,8 @@ hipError_t launch_prep_verify(const Plan& p, const int64_t* eri, const WsView& w
 
 // Producer: chunk c's m-tiles x all column tiles -> ring rows.
 bool produce_uses_dma(const Plan& p, bool aligned);
+hipError_t launch_produce_sweep(const Plan& p, int chunk, const void* grad_y, const void* weight,
+                                bool aligned, const WsView& w, hipStream_t s);
 hipError_t launch_produce_dma(const Plan& p, int chunk, const void* grad_y, const void* weight,
                               const WsView& w, hipStream_t s);
 hipError_t launch_produce(const Plan& p, int chunk, const void* grad_y, const void* weight,

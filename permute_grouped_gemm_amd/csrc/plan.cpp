@@ -29,12 +29,13 @@ size_t ring_budget() {
 
 struct TileShape { int bm, bn; };
 
-// Output tile per regime: large-M MFMA tiles, narrow tiles that spread the
-// weight stream over many workgroups when experts hold few rows, fp32 tiles.
+// Output tile per regime: large-M MFMA tiles; for few rows per expert, m-tiles
+// of 32 rows crossed with units of 16 weight rows that a persistent grid
+// streams in address order; fp32 tiles.
 TileShape tile_shape(int32_t regime) {
   switch (regime) {
     case kLarge: return {256, 256};
-    case kStream: return {32, 64};
+    case kStream: return {32, 16};
     default: return {128, 128};
   }
 }

@@ -89,6 +89,19 @@ def test_many_chunks_bit_exact(orc, monkeypatch):
     np.testing.assert_array_equal(bits(got), bits(orc.case_dx(case, mode=orc.SLOT)))
 
 
+def test_many_chunks_stream_bit_exact(orc, monkeypatch):
+    # few rows per expert (weight-sweep producer) split over many chunks,
+    # with one expert above 32 rows so its m-tiles straddle chunks
+    monkeypatch.setenv("PGG_RING_MB", "1")
+    case = synth.make_case(64, 8, 16, 2048, 1024, "bf16", seed=203, integer=True, routing="heavy",
+                           heavy=4, heavy_rows=60)
+    gy, w, eri, gl = upload(case)
+    plan = pgg.plan(gy, w, eri, gl, case.batch, case.topk, 0)
+    assert plan["regime"] == 1 and plan["max_chunks"] >= 4, plan
+    got = run(case, tensors=(gy, w, eri, gl))
+    np.testing.assert_array_equal(bits(got), bits(orc.case_dx(case, mode=orc.SLOT)))
+
+
 def test_many_chunks_float(orc, monkeypatch):
     monkeypatch.setenv("PGG_RING_MB", "2")
     case = synth.make_case(900, 4, 12, 768, 512, "f16", seed=202, w_std=0.02, name="chunked")
