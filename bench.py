@@ -3,7 +3,9 @@
 
 One step = one fused call (index preparation, grouped-GEMM producer, ordered
 scatter-add consumer) over a seeded synthetic batch whose inputs are already
-resident in HBM.  Prints one JSON line.
+resident in HBM.  Prints one JSON line.  After the W warm-up steps, untimed
+steps continue until 30 ms of work have run, so the timed steps see the GPU's
+steady-state clocks.
 
 Default workload: decode-sized bf16 (batch 16, topK 8, G 16 with 4 empty
 experts, K 7168, N 4096), where streaming the non-empty experts' weights
@@ -11,9 +13,10 @@ dominates; `value` is its effective GB/s.  The same line carries the large
 fp16 workload (batch 13824, topK 8, G 60, K 7168, N 2048; TFLOP/s) under
 "large" unless --no-large is given.
 
-Per-kernel durations come from HIP events the library records around every
-kernel it launches (on the stream the kernels run on), inside the timed
-region.  The CPU baseline is the oracle on a bounded sample of the same
+The roofline's kernel duration comes from HIP events around back-to-back
+launches of that kernel alone (pgg_moe_dx_kernel_time, on the stream the
+calls use); an event pair around each launch inside the calls would add the
+launch's dispatch latency to every measurement.  The CPU baseline is the oracle on a bounded sample of the same
 workload, timed on this host.
 """
 from __future__ import annotations
@@ -30,11 +33,15 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}
+SETTLE_S = 0.03
 METRIC = "fused d_x TFLOP/s (% bf16 MFMA peak) and GB/s (% HBM) at M=110K and M=128"
 
 
-KERNEL_SOURCES = ["permute_grouped_gemm_amd/csrc/gemm.hip", "permute_grouped_gemm_amd/csrc/pgg_internal.h",
-                  "permute_grouped_gemm_amd/csrc/plan.cpp"]
+def kernel_sources():
+    """Every source of the library: a counter run is valid only for the sources it was taken on."""
+    d = os.path.join(ROOT, "permute_grouped_gemm_amd", "csrc")
+    return sorted(os.path.join("permute_grouped_gemm_amd", "csrc", f) for f in os.listdir(d)
+                  if f.endswith((".hip", ".cpp", ".h")))
 
 
 def measured_traffic(kernel, workload):
@@ -45,7 +52,7 @@ def measured_traffic(kernel, workload):
         with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
             table = json.load(f)
         h = hashlib.sha256()
-        for src in KERNEL_SOURCES:
+        for src in kernel_sources():
             with open(os.path.join(ROOT, src), "rb") as f:
                 h.update(f.read())
     except OSError:
@@ -102,6 +109,15 @@ def measure(name, steps, warmup, cpu_baseline, log):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    # settle: the GPU's clocks take a few milliseconds of sustained load to
+    # reach steady state (kernel durations drift by up to ~15% in the first
+    # ~10 ms of back-to-back work), so untimed steps continue until 30 ms of
+    # work have run
+    t_settle = time.time()
+    while time.time() - t_settle < SETTLE_S:
+        for _ in range(4):
+            step()
+        torch.cuda.synchronize()
     code, detail = pgg.read_device_error(ws)
     if code != 0:
         raise RuntimeError(f"device error {code} ({detail})")
@@ -116,34 +132,38 @@ def measure(name, steps, warmup, cpu_baseline, log):
     stop.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(stop) / steps
-    # timed region 2: the same calls with HIP events around every kernel -> roofline
+    # timed region 2: the producer (the dominant kernel) and the consumer, each
+    # launched back to back between two HIP events on the stream the calls use
+    # (after one full call that fills the workspace tables) -> roofline
+    p_ms, p_launches = pgg.kernel_time(gy, w, eri, gl, case.batch, case.topk, case.row_idx_type,
+                                       which="produce", repeats=steps, out=out, workspace=ws)
+    c_ms, c_launches = pgg.kernel_time(gy, w, eri, gl, case.batch, case.topk, case.row_idx_type,
+                                       which="consume", repeats=steps, out=out, workspace=ws)
+    # per-kernel breakdown with an event pair around every launch (each pair
+    # adds the launch's dispatch latency; informative only)
     launches_per_call = 4 + 2 * plan["max_chunks"]
     with pgg.KernelTimer(capacity=launches_per_call * steps + 16) as timer:
-        torch.cuda.synchronize()
-        start.record()
         for _ in range(steps):
             step()
-        stop.record()
         torch.cuda.synchronize()
-    ms_instrumented = start.elapsed_time(stop) / steps
-    log(f"[bench] {name}: {ms * 1e3:.1f} us/step ({ms_instrumented * 1e3:.1f} with kernel events); "
-        f"kernels {timer.result}")
+    log(f"[bench] {name}: {ms * 1e3:.1f} us/step; producer {p_ms * 1e3:.1f} us x {p_launches}, "
+        f"consumer {c_ms * 1e3:.1f} us x {c_launches} per call (back to back); "
+        f"event-bracketed kernels {timer.result}")
 
     flops, bytes_, producer_bytes = algorithmic(case)
     prod_name = {0: "produce_large", 1: "produce_stream", 2: "produce_f32"}[plan["regime"]]
-    p_launches, p_ms = timer.result.get(prod_name, (0, float("nan")))
-    p_ms_per_call = p_ms / steps
-    avg_launch_ms = p_ms / max(1, p_launches)
     hbm_bound = plan["regime"] == 1
     if hbm_bound:
-        achieved = producer_bytes / (p_ms_per_call * 1e-3) / 1e9
+        # algorithmic bytes of one launch: d_y and the non-empty experts' weights
+        achieved = producer_bytes / p_launches / (p_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS, "traffic": None}
         value = bytes_ / (ms * 1e-3) / 1e9
         unit = "GB/s"
     else:
+        # algorithmic flops of one launch: 2 M N K over the call's chunks
         peak = PEAK_TFLOPS[case.dtype]
-        achieved = flops / (p_ms_per_call * 1e-3) / 1e12
+        achieved = flops / p_launches / (p_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                 "frac": achieved / peak, "traffic": None}
         value = flops / (ms * 1e-3) / 1e12
@@ -152,16 +172,17 @@ def measure(name, steps, warmup, cpu_baseline, log):
     roof["traffic"] = traffic
     roof["traffic_unit"] = "bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
     roof["kernel"] = prod_name
-    roof["avg_launch_us"] = avg_launch_ms * 1e3
-    roof["launches_per_step"] = p_launches / steps
+    roof["avg_launch_us"] = p_ms * 1e3
+    roof["launches_per_step"] = p_launches
 
     res = {
-        "value": value, "unit": unit, "ms_per_step": ms, "ms_per_step_instrumented": ms_instrumented,
+        "value": value, "unit": unit, "ms_per_step": ms,
         "tflops": flops / (ms * 1e-3) / 1e12, "gbs": bytes_ / (ms * 1e-3) / 1e9,
         "frac_bf16_peak": flops / (ms * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"],
         "frac_hbm": bytes_ / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "roofline": roof,
-        "kernels_ms_per_step": {k: v[1] / steps for k, v in timer.result.items()},
+        "kernels_ms_per_step": {prod_name: p_ms * p_launches, "consume": c_ms * c_launches},
+        "kernels_event_bracketed_ms_per_step": {k: v[1] / steps for k, v in timer.result.items()},
         "workspace_bytes": plan["workspace_bytes"], "ring_bytes": plan["ring_bytes"],
         "d_expanded_x_fp32_bytes": case.M * case.K * 4,
         "plan": plan,
@@ -229,8 +250,8 @@ def calibrate_copy(log, mib=1024, reps=5):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode_bf16")
     ap.add_argument("--no-large", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -265,15 +286,16 @@ def main():
     if "cpu_baseline" in primary:
         line["cpu_baseline"] = primary["cpu_baseline"]
     line["detail"] = {k: primary[k] for k in ("tflops", "gbs", "frac_bf16_peak", "frac_hbm",
-                                              "ms_per_step_instrumented",
-                                              "kernels_ms_per_step", "workspace_bytes", "ring_bytes",
+                                              "kernels_ms_per_step",
+                                              "kernels_event_bracketed_ms_per_step",
+                                              "workspace_bytes", "ring_bytes",
                                               "d_expanded_x_fp32_bytes", "plan")}
     if not args.no_large and args.workload != "large_f16":
         large = measure("large_f16", max(5, args.steps // 2), args.warmup,
                         not args.no_cpu_baseline, log)
-        line["large"] = {k: large[k] for k in ("value", "unit", "ms_per_step",
-                                               "ms_per_step_instrumented", "tflops", "gbs",
+        line["large"] = {k: large[k] for k in ("value", "unit", "ms_per_step", "tflops", "gbs",
                                                "frac_bf16_peak", "roofline", "kernels_ms_per_step",
+                                               "kernels_event_bracketed_ms_per_step",
                                                "workspace_bytes", "ring_bytes",
                                                "d_expanded_x_fp32_bytes", "config", "dtype")}
         if "cpu_baseline" in large:

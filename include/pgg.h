@@ -179,6 +179,26 @@ typedef struct {
 pgg_status pgg_timing_begin(int32_t capacity);
 pgg_status pgg_timing_end(pgg_kernel_time* out, int32_t max_out, int32_t* n_out);
 
+/*
+ * Kernel benchmark hook.  Runs one full pgg_moe_dx call (same arguments and
+ * contract), which fills the workspace tables, then launches one kernel of
+ * the path back to back, `repeats` times per chunk of the call (which = 0:
+ * the producer, the grouped-matmul stage; which = 1: the consumer, the
+ * routing scatter-add), between two HIP events on `stream`, waits, and
+ * returns the average duration of one launch in *avg_ms and the number of
+ * such launches one pgg_moe_dx call makes in *launches_per_call (may be
+ * NULL).  Back-to-back launches hide the dispatch latency a per-launch event
+ * pair would add to a kernel of ~100 us.  The repeated launches rewrite the
+ * ring and (which = 1) grad_x with the same values.  Creates two events (it
+ * allocates).  Errors: those of pgg_moe_dx; PGG_ERR_INVALID_ARG for which
+ * outside {0, 1}, repeats <= 0 or avg_ms NULL.
+ */
+pgg_status pgg_moe_dx_kernel_time(const pgg_moe_dx_desc* desc, const void* grad_y,
+                                  const void* weight, const int64_t* expanded_row_idx,
+                                  const int64_t* group_list, float* grad_x, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream, int32_t which,
+                                  int32_t repeats, double* avg_ms, int32_t* launches_per_call);
+
 const char* pgg_status_string(pgg_status status);
 const char* pgg_device_error_string(int32_t code);
 

@@ -90,6 +90,8 @@ def lib():
         L.pgg_moe_dx_debug_tables.argtypes = [PD, vp, vp, vp, vp]
         L.pgg_moe_dx_debug_tiles.argtypes = [PD, vp, vp, vp, i32, ctypes.POINTER(i32)]
         L.pgg_moe_dx_plan.argtypes = [PD, ctypes.POINTER(Plan)]
+        L.pgg_moe_dx_kernel_time.argtypes = [PD, vp, vp, vp, vp, vp, vp, sz, vp, i32, i32,
+                                              ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32)]
         L.pgg_timing_begin.argtypes = [i32]
         L.pgg_timing_end.argtypes = [ctypes.POINTER(KernelTime), i32, ctypes.POINTER(i32)]
         L.pgg_status_string.argtypes = [ctypes.c_int]
@@ -234,6 +236,30 @@ def debug_tiles(grad_y, weight, expanded_row_idx, group_list, batch, topk, row_i
     _check(lib().pgg_moe_dx_debug_tiles(ctypes.byref(d), workspace.data_ptr(), _stream_handle(stream),
                                         buf.data_ptr(), cap, ctypes.byref(n)), "debug_tiles")
     return buf[: 3 * n.value].reshape(-1, 3)
+
+
+def kernel_time(grad_y, weight, expanded_row_idx, group_list, batch, topk, row_idx_type=0, *,
+                which: str = "produce", repeats: int = 10, out=None, workspace=None,
+                stream=None) -> Tuple[float, int]:
+    """(average ms of one launch, launches per call) of the producer
+    (``which="produce"``) or the consumer (``"consume"``), launched back to
+    back between two HIP events after one full call (pgg_moe_dx_kernel_time)."""
+    d = _desc_from_tensors(grad_y, weight, expanded_row_idx, group_list, batch, topk, row_idx_type)
+    dev = grad_y.device
+    if workspace is None:
+        workspace = torch.empty(workspace_size_desc(d), dtype=torch.uint8, device=dev)
+    if out is None:
+        out = torch.empty((int(batch), int(weight.shape[1])), dtype=torch.float32, device=dev)
+    avg = ctypes.c_double()
+    n = ctypes.c_int32()
+    w = {"produce": 0, "consume": 1}[which]
+    _check(lib().pgg_moe_dx_kernel_time(ctypes.byref(d), grad_y.data_ptr(), weight.data_ptr(),
+                                        expanded_row_idx.data_ptr(), group_list.data_ptr(),
+                                        out.data_ptr(), workspace.data_ptr(),
+                                        workspace.numel() * workspace.element_size(),
+                                        _stream_handle(stream), w, int(repeats), ctypes.byref(avg),
+                                        ctypes.byref(n)), "kernel_time")
+    return avg.value, n.value
 
 
 class KernelTimer:

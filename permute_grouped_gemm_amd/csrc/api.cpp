@@ -56,6 +56,82 @@ bool is_aligned(const void* ptr, size_t a) { return reinterpret_cast<uintptr_t>(
 
 size_t elem_size(int32_t dtype) { return dtype == PGG_F32 ? 4 : 2; }
 
+struct Call {
+  Plan plan;
+  WsView w;
+  bool aligned;
+};
+
+pgg_status check_call(const pgg_moe_dx_desc* desc, const void* grad_y, const void* weight,
+                      const int64_t* expanded_row_idx, const int64_t* group_list,
+                      const float* grad_x, void* workspace, size_t workspace_bytes, Call* c) {
+  Plan& p = c->plan;
+  const pgg_status st = make_plan(desc, &p);
+  if (st != PGG_OK) return st;
+  if (!grad_y || !weight || !expanded_row_idx || !group_list || !grad_x || !workspace)
+    return PGG_ERR_INVALID_ARG;
+  if (workspace_bytes < p.total) return PGG_ERR_WORKSPACE_TOO_SMALL;
+  if (!is_aligned(workspace, kWorkspaceAlign)) return PGG_ERR_MISALIGNED;
+  if (!is_aligned(expanded_row_idx, 8) || !is_aligned(group_list, 8) || !is_aligned(grad_x, 4) ||
+      !is_aligned(grad_y, elem_size(p.dtype)) || !is_aligned(weight, elem_size(p.dtype)))
+    return PGG_ERR_MISALIGNED;
+
+  const bool aligned = is_aligned(grad_y, 16) && is_aligned(weight, 16) &&
+                       (size_t(p.N) * elem_size(p.dtype)) % 16 == 0;
+  c->aligned = aligned;
+  c->w = ws_view(p, workspace);
+  return PGG_OK;
+}
+
+pgg_status enqueue(const Call& c, const void* grad_y, const void* weight,
+                   const int64_t* expanded_row_idx, const int64_t* group_list, float* grad_x,
+                   hipStream_t stream) {
+  const Plan& p = c.plan;
+  const WsView& w = c.w;
+  const bool aligned = c.aligned;
+  hipError_t e = hipSuccess;
+  if (sweep_can_prepare(p, aligned)) {
+    // one chunk of few rows per expert: the producer launch prepares too
+    {
+      TimedLaunch t(produce_kernel_name(p), stream);
+      e = launch_produce_sweep_prepared(p, grad_y, weight, expanded_row_idx, group_list, w, stream);
+    }
+    if (e == hipSuccess) {
+      TimedLaunch t("consume", stream);
+      e = launch_consume(p, 0, w, grad_x, stream);
+    }
+    return e == hipSuccess ? PGG_OK : PGG_ERR_HIP;
+  }
+  if (p.fused_prep) {
+    TimedLaunch t("prep_fused", stream);
+    e = launch_prep_fused(p, expanded_row_idx, group_list, w, stream);
+  } else {
+    {
+      TimedLaunch t("prep_groups", stream);
+      e = launch_prep_groups(p, group_list, w, stream);
+    }
+    if (e == hipSuccess) {
+      TimedLaunch t("prep_index", stream);
+      e = launch_prep_index(p, expanded_row_idx, w, stream);
+    }
+    if (e == hipSuccess) {
+      TimedLaunch t("prep_verify", stream);
+      e = launch_prep_verify(p, expanded_row_idx, w, stream);
+    }
+  }
+  const char* pname = produce_kernel_name(p);
+  for (int ch = 0; ch < p.max_chunks && e == hipSuccess; ++ch) {
+    {
+      TimedLaunch t(pname, stream);
+      e = launch_produce(p, ch, grad_y, weight, aligned, w, stream);
+    }
+    if (e != hipSuccess) break;
+    TimedLaunch t("consume", stream);
+    e = launch_consume(p, ch, w, grad_x, stream);
+  }
+  return e == hipSuccess ? PGG_OK : PGG_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -91,50 +167,54 @@ pgg_status pgg_moe_dx_plan(const pgg_moe_dx_desc* desc, pgg_plan* out) {
 pgg_status pgg_moe_dx(const pgg_moe_dx_desc* desc, const void* grad_y, const void* weight,
                       const int64_t* expanded_row_idx, const int64_t* group_list, float* grad_x,
                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  Plan p;
-  const pgg_status st = make_plan(desc, &p);
+  Call c;
+  const pgg_status st = check_call(desc, grad_y, weight, expanded_row_idx, group_list, grad_x,
+                                   workspace, workspace_bytes, &c);
   if (st != PGG_OK) return st;
-  if (!grad_y || !weight || !expanded_row_idx || !group_list || !grad_x || !workspace)
-    return PGG_ERR_INVALID_ARG;
-  if (workspace_bytes < p.total) return PGG_ERR_WORKSPACE_TOO_SMALL;
-  if (!is_aligned(workspace, kWorkspaceAlign)) return PGG_ERR_MISALIGNED;
-  if (!is_aligned(expanded_row_idx, 8) || !is_aligned(group_list, 8) || !is_aligned(grad_x, 4) ||
-      !is_aligned(grad_y, elem_size(p.dtype)) || !is_aligned(weight, elem_size(p.dtype)))
-    return PGG_ERR_MISALIGNED;
+  return enqueue(c, grad_y, weight, expanded_row_idx, group_list, grad_x, stream);
+}
 
-  const bool aligned = is_aligned(grad_y, 16) && is_aligned(weight, 16) &&
-                       (size_t(p.N) * elem_size(p.dtype)) % 16 == 0;
-  const WsView w = ws_view(p, workspace);
-
-  hipError_t e = hipSuccess;
-  if (p.fused_prep) {
-    TimedLaunch t("prep_fused", stream);
-    e = launch_prep_fused(p, expanded_row_idx, group_list, w, stream);
-  } else {
-    {
-      TimedLaunch t("prep_groups", stream);
-      e = launch_prep_groups(p, group_list, w, stream);
-    }
-    if (e == hipSuccess) {
-      TimedLaunch t("prep_index", stream);
-      e = launch_prep_index(p, expanded_row_idx, w, stream);
-    }
-    if (e == hipSuccess) {
-      TimedLaunch t("prep_verify", stream);
-      e = launch_prep_verify(p, expanded_row_idx, w, stream);
+pgg_status pgg_moe_dx_kernel_time(const pgg_moe_dx_desc* desc, const void* grad_y,
+                                  const void* weight, const int64_t* expanded_row_idx,
+                                  const int64_t* group_list, float* grad_x, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream, int32_t which,
+                                  int32_t repeats, double* avg_ms, int32_t* launches_per_call) {
+  if ((which != 0 && which != 1) || repeats <= 0 || !avg_ms) return PGG_ERR_INVALID_ARG;
+  Call c;
+  pgg_status st = check_call(desc, grad_y, weight, expanded_row_idx, group_list, grad_x, workspace,
+                             workspace_bytes, &c);
+  if (st != PGG_OK) return st;
+  // one full call fills the workspace tables the kernels read
+  st = enqueue(c, grad_y, weight, expanded_row_idx, group_list, grad_x, stream);
+  if (st != PGG_OK) return st;
+  const Plan& p = c.plan;
+  const bool prepared = sweep_can_prepare(p, c.aligned);
+  hipEvent_t ev[2] = {nullptr, nullptr};
+  for (auto& e : ev)
+    if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) st = PGG_ERR_HIP;
+  hipError_t e = st == PGG_OK ? hipEventRecord(ev[0], stream) : hipErrorUnknown;
+  for (int32_t r = 0; r < repeats && e == hipSuccess; ++r) {
+    for (int ch = 0; ch < p.max_chunks && e == hipSuccess; ++ch) {
+      if (which == 1)
+        e = launch_consume(p, ch, c.w, grad_x, stream);
+      else if (prepared)
+        e = launch_produce_sweep_prepared(p, grad_y, weight, expanded_row_idx, group_list, c.w,
+                                          stream);
+      else
+        e = launch_produce(p, ch, grad_y, weight, c.aligned, c.w, stream);
     }
   }
-  const char* pname = produce_kernel_name(p);
-  for (int c = 0; c < p.max_chunks && e == hipSuccess; ++c) {
-    {
-      TimedLaunch t(pname, stream);
-      e = launch_produce(p, c, grad_y, weight, aligned, w, stream);
-    }
-    if (e != hipSuccess) break;
-    TimedLaunch t("consume", stream);
-    e = launch_consume(p, c, w, grad_x, stream);
-  }
-  return e == hipSuccess ? PGG_OK : PGG_ERR_HIP;
+  if (e == hipSuccess) e = hipEventRecord(ev[1], stream);
+  if (e == hipSuccess) e = hipEventSynchronize(ev[1]);
+  float ms = 0.0f;
+  if (e == hipSuccess) e = hipEventElapsedTime(&ms, ev[0], ev[1]);
+  for (auto& x : ev)
+    if (x) (void)hipEventDestroy(x);
+  if (st != PGG_OK) return st;
+  if (e != hipSuccess) return PGG_ERR_HIP;
+  *avg_ms = double(ms) / (double(repeats) * double(p.max_chunks));
+  if (launches_per_call) *launches_per_call = p.max_chunks;
+  return PGG_OK;
 }
 
 pgg_status pgg_moe_dx_read_device_error(const void* workspace, hipStream_t stream, int32_t* code,
@@ -203,9 +283,11 @@ pgg_status pgg_timing_begin(int32_t capacity) {
   g_timing.start.assign(static_cast<size_t>(capacity), nullptr);
   g_timing.stop.assign(static_cast<size_t>(capacity), nullptr);
   g_timing.names.assign(static_cast<size_t>(capacity), nullptr);
+  // timing-only events: no system-scope fence on record (it would write back
+  // and invalidate the caches between the kernels being timed)
   for (int32_t i = 0; i < capacity; ++i) {
-    if (hipEventCreate(&g_timing.start[i]) != hipSuccess ||
-        hipEventCreate(&g_timing.stop[i]) != hipSuccess)
+    if (hipEventCreateWithFlags(&g_timing.start[i], hipEventDisableSystemFence) != hipSuccess ||
+        hipEventCreateWithFlags(&g_timing.stop[i], hipEventDisableSystemFence) != hipSuccess)
       return PGG_ERR_HIP;
   }
   g_timing.used = 0;

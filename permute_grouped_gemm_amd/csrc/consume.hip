@@ -93,37 +93,37 @@ __global__ __launch_bounds__(kConsumeThreads) void consume_kernel(ConsumeArgs a)
 
 // The whole problem is one chunk: every token's rows are all in the ring, so
 // token b simply adds its topK rows in slot order onto +0.  One workgroup per
-// (token, column block).
+// (token, column block).  Slots are taken kBatch at a time: their row indices
+// and then their rows are all requested before the first addition, so a
+// token costs two memory latencies per batch instead of two per slot; the
+// additions still run in slot order.
+constexpr int kBatch = 8;
+
 template <int VEC>
 __global__ __launch_bounds__(kConsumeThreads) void consume_tokens_kernel(ConsumeArgs a) {
+  typedef float vec_t __attribute__((ext_vector_type(VEC)));
   if (a.hdr->err != kNoError) return;
   const int64_t b = blockIdx.x / a.col_blocks;
   const int cb = static_cast<int>(blockIdx.x - b * a.col_blocks);
   const int64_t k = (static_cast<int64_t>(cb) * kConsumeThreads + threadIdx.x) * VEC;
   if (k >= a.K) return;
   const int32_t* __restrict__ slots = a.inv + b * a.topk;
-  float acc[VEC];
+  vec_t acc = vec_t(0.0f);
+  for (int64_t j0 = 0; j0 < a.topk; j0 += kBatch) {
+    int64_t row[kBatch];
 #pragma unroll
-  for (int v = 0; v < VEC; ++v) acc[v] = 0.0f;
-  for (int64_t j = 0; j < a.topk; ++j) {
-    const int64_t ij = slots[j];
-    if (ij < 0 || ij >= a.M) continue;
-    const float* __restrict__ src = a.ring + ij * a.K + k;
-    if constexpr (VEC == 4) {
-      const float4 s = *reinterpret_cast<const float4*>(src);
-      acc[0] += s.x; acc[1] += s.y; acc[2] += s.z; acc[3] += s.w;
-    } else {
+    for (int q = 0; q < kBatch; ++q) row[q] = j0 + q < a.topk ? slots[j0 + q] : -1;
+    vec_t v[kBatch];
 #pragma unroll
-      for (int v = 0; v < VEC; ++v) acc[v] += src[v];
+    for (int q = 0; q < kBatch; ++q) {
+      const bool ok = row[q] >= 0 && row[q] < a.M;
+      v[q] = ok ? *reinterpret_cast<const vec_t*>(a.ring + row[q] * a.K + k) : vec_t(0.0f);
     }
-  }
-  float* __restrict__ out = a.dx + b * a.K + k;
-  if constexpr (VEC == 4) {
-    *reinterpret_cast<float4*>(out) = make_float4(acc[0], acc[1], acc[2], acc[3]);
-  } else {
 #pragma unroll
-    for (int v = 0; v < VEC; ++v) out[v] = acc[v];
+    for (int q = 0; q < kBatch; ++q)
+      if (row[q] >= 0 && row[q] < a.M) acc += v[q];
   }
+  *reinterpret_cast<vec_t*>(a.dx + b * a.K + k) = acc;
 }
 
 }  // namespace

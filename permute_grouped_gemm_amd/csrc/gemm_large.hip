@@ -26,7 +26,7 @@
 // slot c ^ ((r >> 1) & 7): the 8 rows of each parity get 8 different slots.
 //
 // Masked-off lanes (rows past the tile's rows, columns past K, reduction past
-// N) load 16 zero bytes from the workspace header instead.  Ring stores are
+// N) load 16 zero bytes from a constant in global memory instead.  Ring stores are
 // non-temporal: the consumer reads them back from memory, not from this L2.
 #include "pgg_device.h"
 
@@ -107,7 +107,7 @@ void produce_large_kernel(LargeArgs a) {
   for (int j = 0; j < kLoadsA; ++j) va |= (r0 + 32 * j < rows ? 1u : 0u) << j;
 #pragma unroll
   for (int j = 0; j < kLoadsB; ++j) vb |= (r0 + 32 * j < cols ? 1u : 0u) << j;
-  const void* zero = a.hdr->zero;
+  const void* zero = &kZero16;
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_offset(lds));
   const int64_t row_step = 32 * N;
 

@@ -36,6 +36,7 @@
 // 16-byte bank groups; a row load or store (16 consecutive chunks per 16
 // lanes) does too.
 #include "pgg_device.h"
+#include "pgg_prep.h"
 
 namespace pgg {
 
@@ -76,6 +77,11 @@ struct SweepArgs {
   float* ring;              // [ring_rows, K]
   int64_t N, K;
   int32_t chunk, tc, nkb;   // nkb: 16-column blocks of K
+  // preparation inside the producer launch (one-chunk plans)
+  const int64_t* eri;
+  const int64_t* gl;
+  PrepArgs prep;
+  WsView ws;
 };
 
 template <class T>
@@ -104,9 +110,9 @@ struct Unit {
 };
 
 template <class E>
-__device__ __forceinline__ Unit<E> make_unit(const SweepArgs& a, int t, int kb, int64_t chunk_base) {
+__device__ __forceinline__ Unit<E> make_unit(const SweepArgs& a, const MTile& tile, int kb,
+                                             int64_t chunk_base) {
   Unit<E> x;
-  const MTile tile = a.tiles[static_cast<int64_t>(a.chunk) * a.tc + t];
   x.rows = tile.rows;
   x.k0 = static_cast<int64_t>(kb) * kSwRows;
   x.cols = static_cast<int>(min<int64_t>(kSwRows, a.K - x.k0));
@@ -146,26 +152,60 @@ __device__ __forceinline__ void finish_unit(const SweepArgs& a, const Unit<E>& x
 
 // ---------------------------------------------------------------- direct-to-LDS
 
-template <class T>
+// FUSED (one-chunk plans): block 0 runs the index preparation (tables, tile
+// table, error word) for the consumer, and the other blocks take their tiles
+// straight from group_list, so no preparation kernel has to finish first.
+// They read neither the error word nor the tile table of this call; they check
+// the group counts themselves (a failing check leaves the reporting to block
+// 0) and the d_y rows they touch are then within [0, M).
+template <class T, bool FUSED>
 __global__ __launch_bounds__(kSwThreads) void sweep_dma_kernel(SweepArgs a) {
   using E = typename T::elem;
   constexpr int EPC = T::kPerChunk;
   __shared__ u32x4_t lds[kDmaStages * kDmaStageSlots];   // per stage: weight slab, then d_y rows
   __shared__ float red[kSwWaves][kSwMS][256];
+  static_assert(sizeof(red) >= 2 * kSwThreads * sizeof(long long), "preparation scratch");
 
-  if (a.hdr->err != kNoError) return;
-  const int tiles_here = min(a.tc, a.hdr->n_tiles - a.chunk * a.tc);
+  int bid = static_cast<int>(blockIdx.x), nwg = static_cast<int>(gridDim.x);
+  int tiles_here;
+  int64_t chunk_base;
+  if constexpr (FUSED) {
+    if (bid == 0) {
+      prep_block(a.prep, a.eri, a.gl, a.ws, reinterpret_cast<long long*>(&red[0][0][0]));
+      return;
+    }
+    --bid;
+    --nwg;
+    // lane g of every wave reads group g (at most 64 groups) and the wave
+    // reduces: total rows, total tiles, any count outside [0, M]
+    const int l = static_cast<int>(threadIdx.x & 63);
+    const int64_t c = l < a.prep.G ? a.gl[l] : 0;
+    const bool bad = __any(c < 0 || c > a.prep.M);
+    int64_t rows = c;
+    int tiles = static_cast<int>((max<int64_t>(c, 0) + 16 * kSwMS - 1) / (16 * kSwMS));
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) {
+      rows += __shfl_xor(rows, d);
+      tiles += __shfl_xor(tiles, d);
+    }
+    if (bad || rows != a.prep.M) return;
+    tiles_here = __builtin_amdgcn_readfirstlane(tiles);
+    chunk_base = 0;
+  } else {
+    if (a.hdr->err != kNoError) return;
+    tiles_here = min(a.tc, a.hdr->n_tiles - a.chunk * a.tc);
+    chunk_base = a.chunk_row0[a.chunk];
+  }
   const int nkb = a.nkb;
-  // unit u = t * nkb + kb; this workgroup takes u = blockIdx.x + j * gridDim.x
-  const int t0 = static_cast<int>(blockIdx.x) / nkb;
+  // unit u = t * nkb + kb; this workgroup takes u = bid + j * nwg
+  const int t0 = bid / nkb;
   if (t0 >= tiles_here) return;
-  const int dq = static_cast<int>(gridDim.x) / nkb;
-  const int dr = static_cast<int>(gridDim.x) - dq * nkb;
+  const int dq = nwg / nkb;
+  const int dr = nwg - dq * nkb;
 
   const int64_t N = a.N;
   const int ns = static_cast<int>((N + kDmaChunks * EPC - 1) / (kDmaChunks * EPC));
   if (ns <= 0) return;   // the plan rejects N <= 0; the stage loop needs a stage
-  const int64_t chunk_base = a.chunk_row0[a.chunk];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -173,7 +213,7 @@ __global__ __launch_bounds__(kSwThreads) void sweep_dma_kernel(SweepArgs a) {
   const int lg = lane >> 4;
   const int sub = lane / kDmaChunks;   // row of a wave instruction this lane loads
   const int ci = lane % kDmaChunks;    // LDS slot it fills
-  const void* zero = a.hdr->zero;
+  const void* zero = &kZero16;
   const uint32_t lds_base = lds_offset(lds);
 
   // step cursor: (tile t, column block kb, stage st)
@@ -182,10 +222,39 @@ __global__ __launch_bounds__(kSwThreads) void sweep_dma_kernel(SweepArgs a) {
     int t, kb, st;
     bool ok;
   };
+  // FUSED: group gc's tiles start at tile tb and its rows at row rb; tiles are
+  // opened in increasing order, so this cursor only moves forward
+  int gc = 0, tb = 0;
+  int64_t rb = 0;
+  auto locate = [&](int t) {
+    MTile tile;
+    for (;;) {
+      const int64_t c = scalar_load_i64(a.gl + gc);
+      const int nt = static_cast<int>((c + 16 * kSwMS - 1) / (16 * kSwMS));
+      if (t < tb + nt) {
+        const int q = t - tb;
+        tile.g = gc;
+        tile.row0 = static_cast<int32_t>(rb + int64_t(q) * 16 * kSwMS);
+        tile.rows = static_cast<int32_t>(min<int64_t>(16 * kSwMS, c - int64_t(q) * 16 * kSwMS));
+        tile.pad = 0;
+        return tile;
+      }
+      tb += nt;
+      rb += c;
+      ++gc;
+    }
+  };
   auto open = [&](Cursor& c) {
     c.ok = c.t < tiles_here;
-    if (c.ok) c.x = make_unit<E>(a, __builtin_amdgcn_readfirstlane(c.t),
-                                 __builtin_amdgcn_readfirstlane(c.kb), chunk_base);
+    if (!c.ok) return;
+    const int t = __builtin_amdgcn_readfirstlane(c.t);
+    const int kb = __builtin_amdgcn_readfirstlane(c.kb);
+    MTile tile;
+    if constexpr (FUSED)
+      tile = locate(t);
+    else
+      tile = scalar_load_tile(a.tiles + (static_cast<int64_t>(a.chunk) * a.tc + t));
+    c.x = make_unit<E>(a, tile, kb, chunk_base);
   };
   auto advance = [&](const Cursor& c) {
     Cursor n = c;
@@ -257,7 +326,7 @@ __global__ __launch_bounds__(kSwThreads) void sweep_dma_kernel(SweepArgs a) {
 
   Cursor c0;
   c0.t = t0;
-  c0.kb = static_cast<int>(blockIdx.x) - t0 * nkb;
+  c0.kb = bid - t0 * nkb;
   c0.st = 0;
   open(c0);
   Cursor c1 = advance(c0);
@@ -311,7 +380,8 @@ __global__ __launch_bounds__(kSwThreads) void sweep_reg_kernel(SweepArgs a) {
 
   auto unit_of = [&](int64_t uu) {
     const int tt = static_cast<int>(uu / a.nkb);
-    return make_unit<E>(a, tt, static_cast<int>(uu - static_cast<int64_t>(tt) * a.nkb), chunk_base);
+    const MTile tile = a.tiles[static_cast<int64_t>(a.chunk) * a.tc + tt];
+    return make_unit<E>(a, tile, static_cast<int>(uu - static_cast<int64_t>(tt) * a.nkb), chunk_base);
   };
   auto load_w = [&](const Unit<E>& x, int st, u32x4_t (&wr)[kRegLoads]) {
     const int64_t n = static_cast<int64_t>(st) * kRegChunks * EPC + lane * EPC;
@@ -401,11 +471,16 @@ __global__ __launch_bounds__(kSwThreads) void sweep_reg_kernel(SweepArgs a) {
 }
 
 template <class T>
-hipError_t launch_typed(const Plan& p, const SweepArgs& args, bool aligned, hipStream_t s) {
+hipError_t launch_typed(const Plan& p, const SweepArgs& args, bool aligned, bool fused, hipStream_t s) {
   const int64_t units = static_cast<int64_t>(p.tc) * p.n_col_tiles;
-  if (aligned) {
+  if (fused) {
+    // block 0 prepares; the others sweep (one slot of the two-per-CU grid
+    // is lent to the preparation for its few microseconds)
+    const dim3 grid(static_cast<unsigned>(std::min<int64_t>(units, kDmaGrid - 1) + 1));
+    hipLaunchKernelGGL((sweep_dma_kernel<T, true>), grid, dim3(kSwThreads), 0, s, args);
+  } else if (aligned) {
     const dim3 grid(static_cast<unsigned>(std::min<int64_t>(units, kDmaGrid)));
-    hipLaunchKernelGGL((sweep_dma_kernel<T>), grid, dim3(kSwThreads), 0, s, args);
+    hipLaunchKernelGGL((sweep_dma_kernel<T, false>), grid, dim3(kSwThreads), 0, s, args);
   } else {
     const dim3 grid(static_cast<unsigned>(std::min<int64_t>(units, kRegGrid)));
     hipLaunchKernelGGL((sweep_reg_kernel<T>), grid, dim3(kSwThreads), 0, s, args);
@@ -413,12 +488,8 @@ hipError_t launch_typed(const Plan& p, const SweepArgs& args, bool aligned, hipS
   return hipGetLastError();
 }
 
-}  // namespace
-
-hipError_t launch_produce_sweep(const Plan& p, int chunk, const void* grad_y, const void* weight,
-                                bool aligned, const WsView& w, hipStream_t s) {
-  if (p.bm != 16 * kSwMS || p.bn != kSwRows) return hipErrorInvalidValue;
-  SweepArgs a;
+SweepArgs sweep_args(const Plan& p, int chunk, const void* grad_y, const void* weight, const WsView& w) {
+  SweepArgs a{};
   a.A = grad_y;
   a.B = weight;
   a.hdr = w.hdr;
@@ -430,11 +501,39 @@ hipError_t launch_produce_sweep(const Plan& p, int chunk, const void* grad_y, co
   a.chunk = chunk;
   a.tc = p.tc;
   a.nkb = p.n_col_tiles;
+  a.prep = prep_args(p);
+  a.ws = w;
+  return a;
+}
+
+hipError_t launch(const Plan& p, const SweepArgs& a, bool aligned, bool fused, hipStream_t s) {
+  if (p.bm != 16 * kSwMS || p.bn != kSwRows) return hipErrorInvalidValue;
   switch (p.dtype) {
-    case PGG_BF16: return launch_typed<TBf16>(p, a, aligned, s);
-    case PGG_F16: return launch_typed<TF16>(p, a, aligned, s);
+    case PGG_BF16: return launch_typed<TBf16>(p, a, aligned, fused, s);
+    case PGG_F16: return launch_typed<TF16>(p, a, aligned, fused, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+}  // namespace
+
+bool sweep_can_prepare(const Plan& p, bool aligned) {
+  return aligned && p.regime == kStream && p.max_chunks == 1 && p.G <= kSweepPrepMaxGroups;
+}
+
+hipError_t launch_produce_sweep(const Plan& p, int chunk, const void* grad_y, const void* weight,
+                                bool aligned, const WsView& w, hipStream_t s) {
+  return launch(p, sweep_args(p, chunk, grad_y, weight, w), aligned, false, s);
+}
+
+hipError_t launch_produce_sweep_prepared(const Plan& p, const void* grad_y, const void* weight,
+                                         const int64_t* eri, const int64_t* gl, const WsView& w,
+                                         hipStream_t s) {
+  if (!sweep_can_prepare(p, true)) return hipErrorInvalidValue;
+  SweepArgs a = sweep_args(p, 0, grad_y, weight, w);
+  a.eri = eri;
+  a.gl = gl;
+  return launch(p, a, true, true, s);
 }
 
 }  // namespace pgg

@@ -95,6 +95,10 @@ __device__ __forceinline__ uint32_t lds_offset(const void* p) {
       reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)p));
 }
 
+// 16 zero bytes in global memory: the source of masked-off direct-to-LDS
+// loads (every lane of such a load reads something; masked lanes read zeros).
+__device__ const u32x4_t kZero16 = {0u, 0u, 0u, 0u};
+
 // Direct global -> LDS load of 16 bytes per lane: lane i's bytes land at LDS
 // byte offset m0 + 16 i.  Issued by inline assembly, so the compiler neither
 // tracks nor waits for it: the waits on the vector-memory counter are explicit
@@ -120,6 +124,33 @@ __device__ __forceinline__ void wait_then_barrier() {
   asm volatile("" ::: "memory");
 }
 
+
+// Wave-uniform loads through the scalar data cache (reads only).  The value
+// lands in scalar registers and is waited for on the scalar/LDS counter, so
+// direct-to-LDS loads in flight on the vector-memory counter are not drained
+// for it (a vector load here would be: that counter completes in order).
+// Kernels that also issue direct-to-LDS loads clobber memory in every asm
+// statement, which stops the compiler from choosing scalar loads itself.
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int64_t scalar_load_i64(const int64_t* p) {
+  i32x2_t v;
+  asm volatile("s_load_dwordx2 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+  return static_cast<int64_t>((static_cast<uint64_t>(static_cast<uint32_t>(v[1])) << 32) |
+                              static_cast<uint32_t>(v[0]));
+}
+
+__device__ __forceinline__ MTile scalar_load_tile(const MTile* p) {
+  i32x4_t v;
+  asm volatile("s_load_dwordx4 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+  MTile t;
+  t.g = v[0];
+  t.row0 = v[1];
+  t.rows = v[2];
+  t.pad = v[3];
+  return t;
+}
 
 // Wait for this wave's LDS operations only, then barrier the workgroup (for
 // data exchanged through LDS while direct-to-LDS loads stay in flight).

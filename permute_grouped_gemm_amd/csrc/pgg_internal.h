@@ -25,8 +25,7 @@ struct alignas(16) WsHeader {
   unsigned long long err;
   int32_t n_tiles;      // m-tiles actually produced by the group pass
   int32_t reserved0;
-  int64_t zero[2];      // 16 zero bytes: the source of masked-off direct-to-LDS loads
-  int64_t reserved[4];
+  int64_t reserved[6];
 };
 
 // One m-tile: up to block_m consecutive expanded rows of one expert.
@@ -104,6 +103,14 @@ hipError_t launch_prep_verify(const Plan& p, const int64_t* eri, const WsView& w
 bool produce_uses_dma(const Plan& p, bool aligned);
 hipError_t launch_produce_sweep(const Plan& p, int chunk, const void* grad_y, const void* weight,
                                 bool aligned, const WsView& w, hipStream_t s);
+// One-chunk weight-sweep plans with aligned rows and few groups: the producer
+// launch also runs the index preparation (in a spare workgroup), replacing
+// the preparation kernel.
+constexpr int64_t kSweepPrepMaxGroups = 64;
+bool sweep_can_prepare(const Plan& p, bool aligned);
+hipError_t launch_produce_sweep_prepared(const Plan& p, const void* grad_y, const void* weight,
+                                         const int64_t* eri, const int64_t* gl, const WsView& w,
+                                         hipStream_t s);
 hipError_t launch_produce_dma(const Plan& p, int chunk, const void* grad_y, const void* weight,
                               const WsView& w, hipStream_t s);
 hipError_t launch_produce(const Plan& p, int chunk, const void* grad_y, const void* weight,
