@@ -207,9 +207,15 @@ def oracle_baseline(case, unit, log):
     # else a prefix sized for roughly 10-30 s of CPU work
     n_tok = case.batch if case.M * case.N * case.K <= 8e9 else 192
     toks = np.arange(n_tok, dtype=np.int64)
+    # a sample shorter than 10 s is repeated until 10 s have run, for a stable rate
+    reps = 0
     t0 = time.time()
-    oracle.case_dx_tokens(case, toks, nthreads=threads)
-    dt = time.time() - t0
+    while True:
+        oracle.case_dx_tokens(case, toks, nthreads=threads)
+        reps += 1
+        if time.time() - t0 >= 10.0:
+            break
+    dt = (time.time() - t0) / reps
     rows = n_tok * case.topk
     s = {"f32": 4, "f16": 2, "bf16": 2}[case.dtype]
     if unit == "GB/s":
@@ -227,11 +233,11 @@ def oracle_baseline(case, unit, log):
         val = b / dt / 1e9
     else:
         val = 2.0 * rows * case.N * case.K / dt / 1e12
-    log(f"[bench] oracle sample: {n_tok} tokens in {dt:.1f}s on {threads} threads")
+    log(f"[bench] oracle sample: {n_tok} tokens, {reps} run(s) of {dt:.2f}s on {threads} threads")
     return {"value": val, "unit": unit, "cores": threads, "kind": "oracle",
-            "seconds": dt,
+            "seconds": dt * reps,
             "sample": f"d_x rows of tokens 0..{n_tok - 1} ({rows} expanded rows, all K columns) "
-                      f"of the same inputs"}
+                      f"of the same inputs, computed {reps} time(s)"}
 
 
 def calibrate_copy(log, mib=1024, reps=5):
