@@ -16,9 +16,11 @@
 // explicit (vector memory operations complete in issue order, and these loads
 // write no register).
 //
-// Per stage and wave (2 x 2 waves, 128 x 128 fp32 accumulators each): four
-// chunk pairs of 16 MFMA 32x32x16; the fragments of the next pair are read
-// while the current pair multiplies, across stage boundaries too.
+// Per stage and wave (2 x 4 waves, two per SIMD, 128 x 64 fp32 accumulators
+// each): four chunk pairs of 8 MFMA 32x32x16; the fragments of the next pair
+// are read while the current pair multiplies, across stage boundaries too.
+// The second wave on each SIMD keeps the matrix unit fed while the other
+// issues its loads or waits on LDS.
 //
 // LDS rows are 128 bytes (8 chunks).  128-bit LDS reads are served 16 lanes
 // at a time over 64 banks (256 bytes = 2 rows); a fragment read puts 16
@@ -35,9 +37,9 @@ namespace pgg {
 namespace {
 
 constexpr int kBM = 256, kBN = 256;
-constexpr int kThreads = 256, kWaves = 4;
+constexpr int kThreads = 512, kWaves = 8;    // two waves per SIMD
 constexpr int kWM = 2;                        // waves along rows
-constexpr int kWTM = 128, kWTN = 128;         // wave tile
+constexpr int kWTM = 128, kWTN = 64;          // wave tile
 constexpr int kFM = kWTM / 32, kFN = kWTN / 32;
 constexpr int kRowChunks = 8;                 // 16-byte chunks per LDS row per stage
 constexpr int kBK = kRowChunks * 8;           // reduction elements per stage
@@ -47,6 +49,7 @@ constexpr int kSlotsA = kBM * kRowChunks;
 constexpr int kSlotsB = kBN * kRowChunks;
 constexpr int kStageSlots = kSlotsA + kSlotsB;
 constexpr int kRowsPerLoad = 64 / kRowChunks;          // rows one wave instruction covers
+constexpr int kLoadRows = kRowsPerLoad * kWaves;       // rows one load index covers across the waves
 constexpr int kLoadsA = kSlotsA / kThreads;            // direct-to-LDS loads per thread per stage
 constexpr int kLoadsB = kSlotsB / kThreads;
 constexpr int kLoadsPerStage = kLoadsA + kLoadsB;
@@ -72,7 +75,7 @@ struct LargeArgs {
 __device__ __forceinline__ int slot_of(int r, int c) { return c ^ ((r >> 1) & 7); }
 
 template <class T>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void produce_large_kernel(LargeArgs a) {
   using E = typename T::elem;
   __shared__ u32x4_t lds[kStages * kStageSlots];
@@ -94,9 +97,9 @@ void produce_large_kernel(LargeArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave % kWM, wn = wave / kWM;
   const int lr = lane & 31, lh = lane >> 5;
-  // Direct-to-LDS load j of this wave fills slots (j*4 + wave)*64 + lane of a
-  // region: row r0 + 32 j (r0 = wave*8 + lane/8), slot lane%8, which holds
-  // chunk (lane%8) ^ ((r0/2)%8) -- the same for every j.
+  // Direct-to-LDS load j of this wave fills slots (j*kWaves + wave)*64 + lane of a
+  // region: row r0 + kLoadRows j (r0 = wave*8 + lane/8), slot lane%8, which
+  // holds chunk (lane%8) ^ ((r0/2)%8) -- the same for every j.
   const int r0 = wave * kRowsPerLoad + (lane >> 3);
   const int dma_c = slot_of(r0, lane & 7);
   const E* pa = static_cast<const E*>(a.A) + (static_cast<int64_t>(tile.row0) + r0) * N + dma_c * 8;
@@ -104,12 +107,12 @@ void produce_large_kernel(LargeArgs a) {
       static_cast<const E*>(a.B) + (static_cast<int64_t>(tile.g) * a.K + col0 + r0) * N + dma_c * 8;
   uint32_t va = 0, vb = 0;   // bit j: load j's row lies inside the tile
 #pragma unroll
-  for (int j = 0; j < kLoadsA; ++j) va |= (r0 + 32 * j < rows ? 1u : 0u) << j;
+  for (int j = 0; j < kLoadsA; ++j) va |= (r0 + kLoadRows * j < rows ? 1u : 0u) << j;
 #pragma unroll
-  for (int j = 0; j < kLoadsB; ++j) vb |= (r0 + 32 * j < cols ? 1u : 0u) << j;
+  for (int j = 0; j < kLoadsB; ++j) vb |= (r0 + kLoadRows * j < cols ? 1u : 0u) << j;
   const void* zero = &kZero16;
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_offset(lds));
-  const int64_t row_step = 32 * N;
+  const int64_t row_step = kLoadRows * N;
 
   auto issue = [&](int kt) {
     const uint32_t base = lds0 + static_cast<uint32_t>((kt % kStages) * kStageSlots * 16);
