@@ -188,9 +188,11 @@ pgg_status pgg_timing_end(pgg_kernel_time* out, int32_t max_out, int32_t* n_out)
  * returns the average duration of one launch in *avg_ms and the number of
  * such launches one pgg_moe_dx call makes in *launches_per_call (may be
  * NULL).  Back-to-back launches hide the dispatch latency a per-launch event
- * pair would add to a kernel of ~100 us.  The repeated launches rewrite the
- * ring and (which = 1) grad_x with the same values.  Creates two events (it
- * allocates).  Errors: those of pgg_moe_dx; PGG_ERR_INVALID_ARG for which
+ * pair would add to a kernel of ~100 us.  Repeated producers rewrite the
+ * ring with the values a call leaves there; repeated consumers work on a ring
+ * that holds only the last chunk, so after them one more full call is
+ * enqueued: grad_x and the workspace end as after pgg_moe_dx.  Creates two
+ * events (it allocates).  Errors: those of pgg_moe_dx; PGG_ERR_INVALID_ARG for which
  * outside {0, 1}, repeats <= 0 or avg_ms NULL.
  */
 pgg_status pgg_moe_dx_kernel_time(const pgg_moe_dx_desc* desc, const void* grad_y,

@@ -262,3 +262,46 @@ def test_large_f32_sampled_and_deterministic(orc, name):
     _sampled(orc, case, first)
     for _ in range(9):
         np.testing.assert_array_equal(bits(run(case, tensors=tensors)), bits(first))
+
+
+# ---------------------------------------------------------------- preparation placement
+
+@pytest.mark.parametrize("G,empty", [(64, (0, 63)), (80, (5,))])
+def test_stream_group_count_around_producer_preparation(orc, G, empty):
+    # up to 64 groups the sweep producer prepares the indices itself; above,
+    # a preparation kernel runs first -- both must give the oracle's result
+    case = synth.make_case(40, 8, G, 512, 256, "bf16", seed=700, empty=empty, name=f"G{G}")
+    gy, w, eri, gl = upload(case)
+    assert pgg.plan(gy, w, eri, gl, case.batch, case.topk, 0)["regime"] == 1
+    _parity(orc, case, run(case, tensors=(gy, w, eri, gl)))
+    ws = torch.empty(pgg.workspace_size(gy, w, eri, gl, case.batch, case.topk, 0),
+                     dtype=torch.uint8, device="cuda")
+    run(case, tensors=(gy, w, eri, gl), workspace=ws)
+    inv, ori = pgg.debug_tables(gy, w, eri, gl, case.batch, case.topk, 0, ws)
+    o_ori, o_inv = orc.index(case.eri, 0)
+    np.testing.assert_array_equal(inv.numpy(), o_inv.astype(np.int32))
+    np.testing.assert_array_equal(ori.numpy(), o_ori.astype(np.int32))
+
+
+# ---------------------------------------------------------------- benchmark hook
+
+@pytest.mark.parametrize("which_case", ["stream", "chunked"])
+def test_kernel_time_hook_keeps_results(orc, which_case, monkeypatch):
+    if which_case == "stream":
+        case = synth.make_case(16, 8, 16, 1024, 512, "bf16", seed=800, empty=(2, 7))
+    else:
+        monkeypatch.setenv("PGG_RING_MB", "1")
+        case = synth.make_case(300, 4, 6, 1024, 256, "f16", seed=801, w_std=0.02)
+    gy, w, eri, gl = upload(case)
+    plan = pgg.plan(gy, w, eri, gl, case.batch, case.topk, 0)
+    ws = torch.empty(plan["workspace_bytes"], dtype=torch.uint8, device="cuda")
+    out = torch.empty((case.batch, case.K), dtype=torch.float32, device="cuda")
+    first = run(case, tensors=(gy, w, eri, gl), workspace=ws, out=out)
+    for which in ("produce", "consume"):
+        ms, launches = pgg.kernel_time(gy, w, eri, gl, case.batch, case.topk, 0, which=which,
+                                       repeats=3, out=out, workspace=ws)
+        assert ms > 0 and launches == plan["max_chunks"], (which, ms, launches)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(bits(out.cpu().numpy()), bits(first))
+    assert pgg.read_device_error(ws) == (pgg.DEV_OK, 0)
+    _parity(orc, case, first)
