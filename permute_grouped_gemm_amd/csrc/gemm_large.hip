@@ -169,12 +169,16 @@ void produce_large_kernel(LargeArgs a) {
       if (q + 1 < kPairs) {
         if (q & 1) load_frags(kt, q + 1, fa0, fb0); else load_frags(kt, q + 1, fa1, fb1);
       } else {
-        // stage kt+1 landed everywhere and every wave is done with stage kt
+        // stage kt+1 landed everywhere and every wave is done with stage kt;
+        // the refill of stage kt's buffer is issued by the first wave of each
+        // SIMD before its last MFMAs of the stage and by the second after
+        // them, so one of the two is always feeding the matrix unit
         wait_then_barrier<0>();
-        issue(kt + kStages);            // refills stage kt's buffer
+        if (wave < kWaves / 2) issue(kt + kStages);
         load_frags(kt + 1, 0, fa0, fb0);
       }
       if (q & 1) mfmas(fa1, fb1); else mfmas(fa0, fb0);
+      if (q + 1 == kPairs && wave >= kWaves / 2) issue(kt + kStages);
     }
   }
   // last stages: nothing more to issue
