@@ -150,6 +150,32 @@ def measure(name, steps, warmup, cpu_baseline, log):
         f"consumer {c_ms * 1e3:.1f} us x {c_launches} per call (back to back); "
         f"event-bracketed kernels {timer.result}")
 
+    # cold variant (HBM-bound workloads): a 512 MiB scrub read before every
+    # call, outside its timing, so the caches hold the scrub instead of the
+    # inputs (a read leaves no dirty lines to write back during the call);
+    # warm calls timed the same way (an event pair per call) for comparison
+    cold = None
+    if plan["regime"] == 1:
+        scrub = torch.ones(128 << 20, dtype=torch.int32, device=dev)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(2 * steps)]
+        for k in range(steps):
+            sink = scrub.sum(dtype=torch.int64)
+            ev[k][0].record()
+            step()
+            ev[k][1].record()
+        for k in range(steps, 2 * steps):
+            ev[k][0].record()
+            step()
+            ev[k][1].record()
+        torch.cuda.synchronize()
+        t = [a.elapsed_time(b) * 1e3 for a, b in ev]
+        med = lambda xs: sorted(xs)[len(xs) // 2]
+        cold = {"cold_us_median": med(t[:steps]), "warm_us_median": med(t[steps:]),
+                "method": "event pair around each call; cold = 512 MiB scrub read before each call"}
+        del scrub
+    sclk = smi_sclk()
+
     flops, bytes_, producer_bytes = algorithmic(case)
     prod_name = {0: "produce_large", 1: "produce_stream", 2: "produce_f32"}[plan["regime"]]
     hbm_bound = plan["regime"] == 1
@@ -183,6 +209,7 @@ def measure(name, steps, warmup, cpu_baseline, log):
         "roofline": roof,
         "kernels_ms_per_step": {prod_name: p_ms * p_launches, "consume": c_ms * c_launches},
         "kernels_event_bracketed_ms_per_step": {k: v[1] / steps for k, v in timer.result.items()},
+        "cold_vs_warm": cold, "smi_sclk_after_timing": sclk,
         "workspace_bytes": plan["workspace_bytes"], "ring_bytes": plan["ring_bytes"],
         "d_expanded_x_fp32_bytes": case.M * case.K * 4,
         "plan": plan,
@@ -240,6 +267,22 @@ def oracle_baseline(case, unit, log):
                       f"of the same inputs, computed {reps} time(s)"}
 
 
+def smi_sclk():
+    """The shader clock rocm-smi reports right after the timed steps (or None)."""
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True,
+                           timeout=15)
+        data = json.loads(r.stdout)
+        card = next(iter(data.values()))
+        for k, v in card.items():
+            if "sclk" in k.lower():
+                return v
+    except Exception:
+        return None
+    return None
+
+
 def calibrate_copy(log, mib=1024, reps=5):
     """A plain device copy of known size, for scaling the HBM byte counters."""
     import torch
@@ -292,6 +335,7 @@ def main():
     if "cpu_baseline" in primary:
         line["cpu_baseline"] = primary["cpu_baseline"]
     line["detail"] = {k: primary[k] for k in ("tflops", "gbs", "frac_bf16_peak", "frac_hbm",
+                                              "cold_vs_warm", "smi_sclk_after_timing",
                                               "kernels_ms_per_step",
                                               "kernels_event_bracketed_ms_per_step",
                                               "workspace_bytes", "ring_bytes",
@@ -300,6 +344,7 @@ def main():
         large = measure("large_f16", max(5, args.steps // 2), args.warmup,
                         not args.no_cpu_baseline, log)
         line["large"] = {k: large[k] for k in ("value", "unit", "ms_per_step", "tflops", "gbs",
+                                               "smi_sclk_after_timing",
                                                "frac_bf16_peak", "roofline", "kernels_ms_per_step",
                                                "kernels_event_bracketed_ms_per_step",
                                                "workspace_bytes", "ring_bytes",
