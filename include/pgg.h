@@ -17,7 +17,8 @@
  * entry point.  The library never allocates, frees or synchronises inside
  * pgg_moe_dx; it only enqueues kernels on the caller's stream.
  *
- * Thread safety: every entry point except the timing hooks is reentrant.
+ * Thread safety: every entry point except pgg_timing_begin / pgg_timing_end
+ * is reentrant.
  * Calls that share a workspace must be ordered by the caller (same stream or
  * explicit events).
  */
@@ -43,7 +44,8 @@ typedef enum {
   PGG_ERR_UNSUPPORTED = 2,          /* valid per the page but beyond this build (e.g. M >= 2^31) */
   PGG_ERR_WORKSPACE_TOO_SMALL = 3,  /* workspace_bytes below pgg_moe_dx_workspace_size */
   PGG_ERR_HIP = 4,                  /* a HIP runtime call failed */
-  PGG_ERR_MISALIGNED = 5            /* workspace pointer not 256-byte aligned */
+  PGG_ERR_MISALIGNED = 5            /* workspace not 256-byte aligned, or an input / output pointer
+                                       not aligned to its element size */
 } pgg_status;
 
 /* Data-dependent errors found on the device (read with
@@ -153,7 +155,10 @@ typedef struct {
   int32_t max_tiles;       /* upper bound on m-tiles: ceil(M/block_m) + G */
   int32_t max_chunks;      /* chunks enqueued per call */
   int32_t ring_rows;       /* rows of one ring buffer */
-  int32_t fused_prep;      /* 1 when index preparation runs as one workgroup */
+  int32_t fused_prep;      /* 1 when index preparation runs in one workgroup: a kernel of its
+                              own, or -- one-chunk weight-streaming plans with G <= 64, when
+                              the rows are 16-byte aligned -- a spare workgroup of the
+                              producer launch; 0: three preparation kernels */
   size_t ring_bytes;       /* fp32 ring */
   size_t table_bytes;      /* index / tile tables and header */
   size_t workspace_bytes;  /* total, as returned by pgg_moe_dx_workspace_size */
@@ -192,8 +197,8 @@ pgg_status pgg_timing_end(pgg_kernel_time* out, int32_t max_out, int32_t* n_out)
  * ring with the values a call leaves there; repeated consumers work on a ring
  * that holds only the last chunk, so after them one more full call is
  * enqueued: grad_x and the workspace end as after pgg_moe_dx.  Creates two
- * events (it allocates).  Errors: those of pgg_moe_dx; PGG_ERR_INVALID_ARG for which
- * outside {0, 1}, repeats <= 0 or avg_ms NULL.
+ * events (it allocates).  Errors: those of pgg_moe_dx; PGG_ERR_INVALID_ARG
+ * for `which` outside {0, 1}, repeats <= 0 or avg_ms NULL.
  */
 pgg_status pgg_moe_dx_kernel_time(const pgg_moe_dx_desc* desc, const void* grad_y,
                                   const void* weight, const int64_t* expanded_row_idx,

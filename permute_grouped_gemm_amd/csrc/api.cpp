@@ -7,8 +7,10 @@
 //   2. for every chunk of m-tiles: the MFMA producer, which writes the
 //      chunk's fp32 rows into the ring, then the ordered consumer, which adds
 //      them into d_x.
-// Stream order carries every dependency; there is no host synchronisation
-// and no allocation on this path.
+// One-chunk weight-streaming calls with aligned rows and few groups take two
+// launches: the producer runs the preparation in a spare workgroup.  Stream
+// order carries every dependency; there is no host synchronisation and no
+// allocation on this path.
 #include <stdio.h>
 #include <string.h>
 

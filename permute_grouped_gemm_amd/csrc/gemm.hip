@@ -34,7 +34,6 @@ namespace pgg {
 
 namespace {
 
-
 struct GemmArgs {
   const void* A;            // grad_y [M, N]
   const void* B;            // weight [G, K, N]

@@ -116,7 +116,6 @@ hipError_t launch_produce_dma(const Plan& p, int chunk, const void* grad_y, cons
 hipError_t launch_produce(const Plan& p, int chunk, const void* grad_y, const void* weight,
                           bool aligned, const WsView& w, hipStream_t s);
 
-
 // Consumer: ordered scatter-add of chunk c's ring rows into d_x.
 hipError_t launch_consume(const Plan& p, int chunk, const WsView& w, float* grad_x,
                           hipStream_t s);
