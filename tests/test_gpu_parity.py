@@ -66,6 +66,9 @@ EXACT_SHAPES = [
          heavy_rows=50),                                    # streaming, one m-tile per pass, 4 passes
     dict(batch=64, topk=8, G=16, K=520, N=264, routing="heavy", empty=(3,), heavy=5,
          heavy_rows=100),                                   # streaming, two m-tiles per pass, K/N tails
+    dict(batch=4, topk=2, G=4, K=5, N=8),                  # streaming: one partial unit, one tiny stage
+    dict(batch=4, topk=2, G=4, K=40, N=24),                # streaming: K not a multiple of 16
+    dict(batch=3, topk=1, G=1, K=16, N=4096),              # streaming: one expert, one unit, 16 stages
 ]
 
 
