@@ -267,11 +267,33 @@ def oracle_baseline(case, unit, log):
                       f"of the same inputs, computed {reps} time(s)"}
 
 
+def under_profiler():
+    """True when a profiler's tool library is preloaded into this process."""
+    pre = os.environ.get("LD_PRELOAD", "")
+    return "rocprof" in pre or any(k.startswith("ROCPROF") for k in os.environ)
+
+
 def smi_sclk():
-    """The shader clock rocm-smi reports right after the timed steps (or None)."""
+    """The shader clock rocm-smi reports right after the timed steps (or None).
+
+    Skipped under a profiler: its preloaded library would initialise the GPU in
+    every child process, and a script launched through a shebang hop would then
+    replace such a process.  rocm-smi is a Python script, so it is started with
+    this interpreter directly rather than through its `#!/usr/bin/env` line.
+    """
+    import shutil
     import subprocess
+    if under_profiler():
+        return None
     try:
-        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True,
+        path = shutil.which("rocm-smi")
+        if path is None:
+            return None
+        path = os.path.realpath(path)
+        with open(path, "rb") as f:
+            first = f.readline()
+        cmd = [sys.executable, path] if b"python" in first else [path]
+        r = subprocess.run(cmd + ["--showclocks", "--json"], capture_output=True, text=True,
                            timeout=15)
         data = json.loads(r.stdout)
         card = next(iter(data.values()))
