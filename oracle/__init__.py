@@ -12,6 +12,11 @@ scatter-add of expanded rows back to their token, batch row = original
 position / topK).  ``brute.py`` evaluates the merged scalar formula of the same
 section literally, with its indicator function, for tiny inputs.
 
+``moe_fwd`` is the forward chain of the same section (MoeInitRouting =
+Permute, then GroupedMatmul): expanded row i copies token p(i) / topK of x,
+and every expert's rows are multiplied by that expert's weight slice, in
+float64, with numpy's matmul as the per-expert product.
+
 Parity status: every function here is pinned by the CPU tests in
 ``tests/test_oracle_*.py`` (brute force, library matmul special cases, the
 adjoint identity against an independent forward, invariants, hand-worked
@@ -211,6 +216,54 @@ def colsum(grad_y, weight, eri, group_list, batch, topk, row_idx_type, dtype, co
     if rc:
         raise OracleError(rc, "colsum")
     return s, a
+
+
+def moe_fwd(x, weight, eri, group_list, batch, topk, row_idx_type, dtype, *, rows=None,
+            want_abs=False):
+    """Forward y[i, n] = sum_k x[p(i) // topK, k] * W[g(i), k, n] in float64.
+
+    MoeInitRoutingGroupedMatmulGrad design page, §数学定义和公式, forward
+    formulas: expanded_x = Permute(x) (row i copies token p(i) // topK, with
+    p(i) the original position of expanded row i), then the grouped matmul of
+    §1.1 step 2, each expert's expanded rows times its weight slice W[g]
+    ([K, N]).  x is [batch, K], weight [G, K, N], both in the storage type
+    ``dtype``; eri, group_list and row_idx_type as for moe_dx.  ``rows``
+    (optional) selects expanded rows; the result has one row per entry.  With
+    want_abs, also returns absdot[i, n] = sum_k |x|·|W| over the same terms.
+    Only the weight slices of experts that own a selected row are decoded.
+    """
+    x = np.ascontiguousarray(x)
+    weight = np.ascontiguousarray(weight)
+    if x.ndim != 2 or weight.ndim != 3:
+        raise OracleError(ERR_SHAPE, "rank")
+    G, K, N = weight.shape
+    M = batch * topk
+    if x.shape != (batch, K) or np.shape(eri) != (M,) or np.shape(group_list) != (G,):
+        raise OracleError(ERR_SHAPE, "shape")
+    off = offsets(group_list, M)
+    ori, _ = index(eri, row_idx_type)
+    sel = np.arange(M, dtype=np.int64) if rows is None else np.asarray(rows, dtype=np.int64)
+    if sel.size and (sel.min() < 0 or sel.max() >= M):
+        raise OracleError(ERR_INDEX_RANGE, "rows")
+    # g(i): the expert whose row range [off[g], off[g+1]) holds i
+    g_of = np.searchsorted(off, sel, side="right") - 1
+    y = np.zeros((sel.size, N), dtype=np.float64)
+    absdot = np.zeros((sel.size, N), dtype=np.float64) if want_abs else None
+    for g in np.unique(g_of):
+        at = np.nonzero(g_of == g)[0]
+        tokens = ori[sel[at]] // topk
+        xg = decode(x[tokens], dtype)
+        wg = decode(weight[g], dtype)
+        y[at] = xg @ wg
+        if want_abs:
+            absdot[at] = np.abs(xg) @ np.abs(wg)
+    return (y, absdot) if want_abs else y
+
+
+def case_fwd(case, x, **kw):
+    """moe_fwd on a ``synth.Case`` and its forward input x [batch, K]."""
+    return moe_fwd(x, case.weight, case.eri, case.group_list, case.batch, case.topk,
+                   case.row_idx_type, case.dtype, **kw)
 
 
 def case_colsum(case, cols, **kw):

@@ -252,6 +252,12 @@ def make_case(batch: int, topk: int, G: int, K: int, N: int, dtype: str = "f32",
 # the five workloads and the white-box matrix
 # ----------------------------------------------------------------------------
 
+def forward_input(case: Case, integer: bool = False, std: float = 1.0) -> np.ndarray:
+    """The forward's token activations x [batch, K] for a case, in its storage
+    type: N(0, std) (or integers in [-2, 2]) from the case's seed, tensor id 3."""
+    return draw_values(case.seed, 3, (case.batch, case.K), case.dtype, std, integer)
+
+
 def _pick_empty(seed: int, G: int, n: int) -> list:
     rng = np.random.Generator(np.random.PCG64(seed + 1000))
     return sorted(int(e) for e in rng.choice(G, size=n, replace=False))
