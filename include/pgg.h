@@ -120,7 +120,8 @@ pgg_status pgg_moe_dx(const pgg_moe_dx_desc* desc, const void* grad_y, const voi
                       hipStream_t stream);
 
 /*
- * Read the device error word of the last pgg_moe_dx that used `workspace`.
+ * Read the device error word of the last pgg_moe_dx (or pgg_moe_fwd) that
+ * used `workspace`.
  * Synchronises `stream`.  *code receives a pgg_device_error; *detail its
  * detail value (may be NULL).  When several violations exist, the one with
  * the smallest (code, detail) is reported, so the report is deterministic.
@@ -205,6 +206,82 @@ pgg_status pgg_moe_dx_kernel_time(const pgg_moe_dx_desc* desc, const void* grad_
                                   const int64_t* group_list, float* grad_x, void* workspace,
                                   size_t workspace_bytes, hipStream_t stream, int32_t which,
                                   int32_t repeats, double* avg_ms, int32_t* launches_per_call);
+
+/*
+ * Forward of the same layer: MoeInitRouting (Permute) followed by
+ * GroupedMatmul (MoeInitRoutingGroupedMatmulGrad design page, §数学定义和公式,
+ * forward formulas; §1.1 steps 1 and 2):
+ *
+ *     expanded_x[i,:] = x[p(i) / topK, :]
+ *     y[i,n]          = sum_k expanded_x[i,k] * W[g(i),k,n]
+ *
+ * with p(i) the original position of expanded row i and g(i) its expert, as
+ * for pgg_moe_dx.  expanded_x is never stored: every output tile gathers its
+ * rows of x directly.  fp32 accumulation; y is float32, always.
+ *
+ *   x                 [x_rows = batch, x_cols = K]                  dtype
+ *   weight            [weight_groups = G, weight_rows = K, weight_cols = N]  dtype
+ *   expanded_row_idx  [idx_len = M = batch * topk]                  int64
+ *   group_list        [group_list_len = G]                          int64
+ *   y (output)        [M, N]                                        float32
+ *
+ * y rows are in expanded (expert-grouped) order: row i belongs to expert g(i).
+ * Constraints checked on the host: x_rows == batch; x_cols == weight_rows;
+ * group_list_len == weight_groups; topk > 0; batch > 0; idx_len ==
+ * batch * topk; row_idx_type in {0, 1}; x_dtype == weight_dtype.
+ */
+typedef struct {
+  int64_t x_rows, x_cols;
+  int64_t weight_groups, weight_rows, weight_cols;
+  int64_t idx_len;
+  int64_t group_list_len;
+  int64_t batch, topk;
+  int32_t row_idx_type;
+  int32_t x_dtype;        /* pgg_dtype */
+  int32_t weight_dtype;   /* pgg_dtype */
+  int32_t reserved;       /* must be 0 */
+} pgg_moe_fwd_desc;
+
+/* Workspace size of the forward (host only; shapes only): O(M + G) integer
+ * index and tile tables, no fp32 buffer. */
+pgg_status pgg_moe_fwd_workspace_size(const pgg_moe_fwd_desc* desc, size_t* bytes);
+
+/*
+ * Enqueue the forward on `stream` (asynchronous; no host sync, no allocation).
+ * x, weight, expanded_row_idx, group_list: device pointers, read only.
+ * y: device pointer to M*N floats; every row of a non-empty expert is fully
+ *   written (with group_list summing to M, that is all of y).  It must not
+ *   alias an input or the workspace.
+ * workspace: device pointer, 256-byte aligned, at least the queried size;
+ *   owned by the caller; contents on entry ignored.
+ * Errors: host-checkable violations return a status before anything is
+ * enqueued (PGG_ERR_MISALIGNED for a workspace not 256-byte aligned or an
+ * input / output pointer not aligned to its element size).  Data-dependent
+ * violations set the workspace's error word, as for pgg_moe_dx (then y is
+ * unspecified); pgg_moe_dx_read_device_error reads it from this workspace
+ * too.  Empty experts' weight slices are never read.
+ */
+pgg_status pgg_moe_fwd(const pgg_moe_fwd_desc* desc, const void* x, const void* weight,
+                       const int64_t* expanded_row_idx, const int64_t* group_list, float* y,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Plan of the forward (host only): regime 0 = 256x256 tiles, 1 = 32-row
+ * m-tiles for few rows per expert, 2 = fp32; tiles_per_chunk = max_tiles,
+ * max_chunks = 1, ring fields 0. */
+pgg_status pgg_moe_fwd_plan(const pgg_moe_fwd_desc* desc, pgg_plan* plan);
+
+/*
+ * Kernel benchmark hook of the forward: one full pgg_moe_fwd call (same
+ * contract), then its grouped-matmul kernel `repeats` times back to back
+ * between two HIP events on `stream`; waits and returns the average duration
+ * of one launch in *avg_ms.  Repeats rewrite y with the same values.  Creates
+ * two events (it allocates).  Errors: those of pgg_moe_fwd;
+ * PGG_ERR_INVALID_ARG for repeats <= 0 or avg_ms NULL.
+ */
+pgg_status pgg_moe_fwd_kernel_time(const pgg_moe_fwd_desc* desc, const void* x, const void* weight,
+                                   const int64_t* expanded_row_idx, const int64_t* group_list,
+                                   float* y, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream, int32_t repeats, double* avg_ms);
 
 const char* pgg_status_string(pgg_status status);
 const char* pgg_device_error_string(int32_t code);

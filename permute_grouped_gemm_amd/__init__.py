@@ -11,6 +11,12 @@ the library is missing, importing the entry points raises.
 computes, for the MoeInitRoutingGroupedMatmulGrad operator (design page,
 §数学定义和公式), d_x[b,k] = sum over expanded rows i of token b of
 sum_n grad_y[i,n] * weight[g(i),k,n], returned as float32 [batch, K].
+
+    y = moe_fwd(x, weight, expanded_row_idx, group_list, topk, row_idx_type)
+
+is the layer's forward (the same section's forward formulas): Permute then
+GroupedMatmul, y[i,n] = sum_k x[p(i) // topK, k] * weight[g(i),k,n], float32
+[M, N] in expanded (expert-grouped) row order.
 """
 from __future__ import annotations
 
@@ -23,6 +29,7 @@ import torch
 
 __all__ = [
     "moe_dx", "workspace_size", "plan", "read_device_error", "debug_tables", "debug_tiles",
+    "moe_fwd", "fwd_workspace_size", "fwd_plan", "fwd_kernel_time",
     "KernelTimer", "PggError", "lib", "LIB_PATH", "HEADER_PATH",
 ]
 
@@ -42,6 +49,17 @@ class Desc(ctypes.Structure):
         ("weight_cols", ctypes.c_int64), ("idx_len", ctypes.c_int64),
         ("group_list_len", ctypes.c_int64), ("batch", ctypes.c_int64), ("topk", ctypes.c_int64),
         ("row_idx_type", ctypes.c_int32), ("grad_y_dtype", ctypes.c_int32),
+        ("weight_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
+    ]
+
+
+class FwdDesc(ctypes.Structure):
+    _fields_ = [
+        ("x_rows", ctypes.c_int64), ("x_cols", ctypes.c_int64),
+        ("weight_groups", ctypes.c_int64), ("weight_rows", ctypes.c_int64),
+        ("weight_cols", ctypes.c_int64), ("idx_len", ctypes.c_int64),
+        ("group_list_len", ctypes.c_int64), ("batch", ctypes.c_int64), ("topk", ctypes.c_int64),
+        ("row_idx_type", ctypes.c_int32), ("x_dtype", ctypes.c_int32),
         ("weight_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
     ]
 
@@ -92,6 +110,12 @@ def lib():
         L.pgg_moe_dx_plan.argtypes = [PD, ctypes.POINTER(Plan)]
         L.pgg_moe_dx_kernel_time.argtypes = [PD, vp, vp, vp, vp, vp, vp, sz, vp, i32, i32,
                                               ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32)]
+        PF = ctypes.POINTER(FwdDesc)
+        L.pgg_moe_fwd_workspace_size.argtypes = [PF, ctypes.POINTER(sz)]
+        L.pgg_moe_fwd.argtypes = [PF, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.pgg_moe_fwd_plan.argtypes = [PF, ctypes.POINTER(Plan)]
+        L.pgg_moe_fwd_kernel_time.argtypes = [PF, vp, vp, vp, vp, vp, vp, sz, vp, i32,
+                                               ctypes.POINTER(ctypes.c_double)]
         L.pgg_timing_begin.argtypes = [i32]
         L.pgg_timing_end.argtypes = [ctypes.POINTER(KernelTime), i32, ctypes.POINTER(i32)]
         L.pgg_status_string.argtypes = [ctypes.c_int]
@@ -100,6 +124,8 @@ def lib():
         L.pgg_device_error_string.restype = ctypes.c_char_p
         for f in ("pgg_moe_dx_workspace_size", "pgg_moe_dx", "pgg_moe_dx_read_device_error",
                   "pgg_moe_dx_debug_tables", "pgg_moe_dx_debug_tiles", "pgg_moe_dx_plan",
+                  "pgg_moe_dx_kernel_time", "pgg_moe_fwd_workspace_size", "pgg_moe_fwd",
+                  "pgg_moe_fwd_plan", "pgg_moe_fwd_kernel_time",
                   "pgg_timing_begin", "pgg_timing_end"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
@@ -262,8 +288,104 @@ def kernel_time(grad_y, weight, expanded_row_idx, group_list, batch, topk, row_i
     return avg.value, n.value
 
 
+# ---------------------------------------------------------------- forward
+
+def make_fwd_desc(x_shape, weight_shape, idx_len, group_list_len, batch, topk, row_idx_type,
+                  x_dtype, weight_dtype) -> FwdDesc:
+    if len(x_shape) != 2 or len(weight_shape) != 3:
+        raise PggError(ERR_INVALID_ARG, "rank")
+    d = FwdDesc()
+    d.x_rows, d.x_cols = (int(v) for v in x_shape)
+    d.weight_groups, d.weight_rows, d.weight_cols = (int(v) for v in weight_shape)
+    d.idx_len = int(idx_len)
+    d.group_list_len = int(group_list_len)
+    d.batch = int(batch)
+    d.topk = int(topk)
+    d.row_idx_type = int(row_idx_type)
+    d.x_dtype = x_dtype
+    d.weight_dtype = weight_dtype
+    d.reserved = 0
+    return d
+
+
+def _fwd_desc_from_tensors(x, weight, eri, group_list, topk, row_idx_type) -> FwdDesc:
+    if eri.dim() != 1 or group_list.dim() != 1 or x.dim() != 2:
+        raise PggError(ERR_INVALID_ARG, "rank")
+    if eri.dtype != torch.int64 or group_list.dtype != torch.int64:
+        raise PggError(ERR_INVALID_ARG, "index dtype")
+    return make_fwd_desc(x.shape, weight.shape, eri.shape[0], group_list.shape[0], x.shape[0], topk,
+                         row_idx_type, DTYPE_CODE.get(x.dtype, -1), DTYPE_CODE.get(weight.dtype, -1))
+
+
+def fwd_workspace_size_desc(d: FwdDesc) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().pgg_moe_fwd_workspace_size(ctypes.byref(d), ctypes.byref(n)), "fwd_workspace_size")
+    return n.value
+
+
+def fwd_workspace_size(x, weight, expanded_row_idx, group_list, topk, row_idx_type=0) -> int:
+    return fwd_workspace_size_desc(_fwd_desc_from_tensors(x, weight, expanded_row_idx, group_list,
+                                                          topk, row_idx_type))
+
+
+def fwd_plan(x, weight, expanded_row_idx, group_list, topk, row_idx_type=0) -> dict:
+    d = _fwd_desc_from_tensors(x, weight, expanded_row_idx, group_list, topk, row_idx_type)
+    p = Plan()
+    _check(lib().pgg_moe_fwd_plan(ctypes.byref(d), ctypes.byref(p)), "fwd_plan")
+    return p.as_dict()
+
+
+def _fwd_buffers(d, x, weight, out, workspace):
+    dev = x.device
+    if workspace is None:
+        workspace = torch.empty(fwd_workspace_size_desc(d), dtype=torch.uint8, device=dev)
+    shape = (int(d.batch * d.topk), int(weight.shape[2]))
+    if out is None:
+        out = torch.empty(shape, dtype=torch.float32, device=dev)
+    if out.dtype != torch.float32 or not out.is_contiguous() or tuple(out.shape) != shape:
+        raise PggError(ERR_INVALID_ARG, "out must be a contiguous float32 [M, N] tensor")
+    return out, workspace
+
+
+def moe_fwd(x: torch.Tensor, weight: torch.Tensor, expanded_row_idx: torch.Tensor,
+            group_list: torch.Tensor, topk: int, row_idx_type: int = 0, *,
+            out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+            stream=None) -> torch.Tensor:
+    """Forward Permute + GroupedMatmul: float32 y [batch*topk, N] (asynchronous).
+
+    x [batch, K] and weight [G, K, N] share one of float32 / float16 /
+    bfloat16; expanded_row_idx [batch*topk] and group_list [G] are int64."""
+    d = _fwd_desc_from_tensors(x, weight, expanded_row_idx, group_list, topk, row_idx_type)
+    for t in (x, weight, expanded_row_idx, group_list):
+        if not t.is_cuda or not t.is_contiguous():
+            raise PggError(ERR_INVALID_ARG, "inputs must be contiguous GPU tensors")
+    out, workspace = _fwd_buffers(d, x, weight, out, workspace)
+    st = lib().pgg_moe_fwd(ctypes.byref(d), x.data_ptr(), weight.data_ptr(),
+                           expanded_row_idx.data_ptr(), group_list.data_ptr(), out.data_ptr(),
+                           workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                           _stream_handle(stream))
+    _check(st, "pgg_moe_fwd")
+    return out
+
+
+def fwd_kernel_time(x, weight, expanded_row_idx, group_list, topk, row_idx_type=0, *,
+                    repeats: int = 10, out=None, workspace=None, stream=None) -> float:
+    """Average ms of one launch of the forward's grouped-matmul kernel, launched
+    back to back after one full call (pgg_moe_fwd_kernel_time)."""
+    d = _fwd_desc_from_tensors(x, weight, expanded_row_idx, group_list, topk, row_idx_type)
+    out, workspace = _fwd_buffers(d, x, weight, out, workspace)
+    avg = ctypes.c_double()
+    _check(lib().pgg_moe_fwd_kernel_time(ctypes.byref(d), x.data_ptr(), weight.data_ptr(),
+                                         expanded_row_idx.data_ptr(), group_list.data_ptr(),
+                                         out.data_ptr(), workspace.data_ptr(),
+                                         workspace.numel() * workspace.element_size(),
+                                         _stream_handle(stream), int(repeats), ctypes.byref(avg)),
+           "fwd_kernel_time")
+    return avg.value
+
+
 class KernelTimer:
-    """Per-kernel HIP-event timing of pgg_moe_dx calls made inside the block."""
+    """Per-kernel HIP-event timing of pgg_moe_dx / pgg_moe_fwd calls made inside the block."""
 
     def __init__(self, capacity: int = 4096):
         self.capacity = capacity

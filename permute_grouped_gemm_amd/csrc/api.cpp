@@ -1,4 +1,5 @@
-// C ABI of the fused MoE d_x backward (declared in include/pgg.h).
+// C ABI of the fused MoE d_x backward and of the layer's forward (declared
+// in include/pgg.h).
 //
 // The execute call validates the descriptor on the host, lays out the
 // workspace, and enqueues on the caller's stream:
@@ -85,6 +86,30 @@ pgg_status check_call(const pgg_moe_dx_desc* desc, const void* grad_y, const voi
   return PGG_OK;
 }
 
+// Index preparation: group offsets, m-tile table, inv/ori, checks.
+hipError_t enqueue_prep(const Plan& p, const int64_t* expanded_row_idx, const int64_t* group_list,
+                        const WsView& w, hipStream_t stream) {
+  hipError_t e = hipSuccess;
+  if (p.fused_prep) {
+    TimedLaunch t("prep_fused", stream);
+    e = launch_prep_fused(p, expanded_row_idx, group_list, w, stream);
+  } else {
+    {
+      TimedLaunch t("prep_groups", stream);
+      e = launch_prep_groups(p, group_list, w, stream);
+    }
+    if (e == hipSuccess) {
+      TimedLaunch t("prep_index", stream);
+      e = launch_prep_index(p, expanded_row_idx, w, stream);
+    }
+    if (e == hipSuccess) {
+      TimedLaunch t("prep_verify", stream);
+      e = launch_prep_verify(p, expanded_row_idx, w, stream);
+    }
+  }
+  return e;
+}
+
 pgg_status enqueue(const Call& c, const void* grad_y, const void* weight,
                    const int64_t* expanded_row_idx, const int64_t* group_list, float* grad_x,
                    hipStream_t stream) {
@@ -104,23 +129,7 @@ pgg_status enqueue(const Call& c, const void* grad_y, const void* weight,
     }
     return e == hipSuccess ? PGG_OK : PGG_ERR_HIP;
   }
-  if (p.fused_prep) {
-    TimedLaunch t("prep_fused", stream);
-    e = launch_prep_fused(p, expanded_row_idx, group_list, w, stream);
-  } else {
-    {
-      TimedLaunch t("prep_groups", stream);
-      e = launch_prep_groups(p, group_list, w, stream);
-    }
-    if (e == hipSuccess) {
-      TimedLaunch t("prep_index", stream);
-      e = launch_prep_index(p, expanded_row_idx, w, stream);
-    }
-    if (e == hipSuccess) {
-      TimedLaunch t("prep_verify", stream);
-      e = launch_prep_verify(p, expanded_row_idx, w, stream);
-    }
-  }
+  e = enqueue_prep(p, expanded_row_idx, group_list, w, stream);
   const char* pname = produce_kernel_name(p);
   for (int ch = 0; ch < p.max_chunks && e == hipSuccess; ++ch) {
     {
@@ -132,6 +141,53 @@ pgg_status enqueue(const Call& c, const void* grad_y, const void* weight,
     e = launch_consume(p, ch, w, grad_x, stream);
   }
   return e == hipSuccess ? PGG_OK : PGG_ERR_HIP;
+}
+
+pgg_status check_fwd(const pgg_moe_fwd_desc* desc, const void* x, const void* weight,
+                     const int64_t* expanded_row_idx, const int64_t* group_list, const float* y,
+                     void* workspace, size_t workspace_bytes, Call* c) {
+  Plan& p = c->plan;
+  const pgg_status st = make_fwd_plan(desc, &p);
+  if (st != PGG_OK) return st;
+  if (!x || !weight || !expanded_row_idx || !group_list || !y || !workspace)
+    return PGG_ERR_INVALID_ARG;
+  if (workspace_bytes < p.total) return PGG_ERR_WORKSPACE_TOO_SMALL;
+  if (!is_aligned(workspace, kWorkspaceAlign)) return PGG_ERR_MISALIGNED;
+  const size_t es = elem_size(p.dtype);
+  if (!is_aligned(expanded_row_idx, 8) || !is_aligned(group_list, 8) || !is_aligned(y, 4) ||
+      !is_aligned(x, es) || !is_aligned(weight, es))
+    return PGG_ERR_MISALIGNED;
+  // x rows hold the reduction (plan N), weight rows the output columns (plan K)
+  c->aligned = is_aligned(x, 16) && is_aligned(weight, 16) && (size_t(p.N) * es) % 16 == 0 &&
+               (size_t(p.K) * es) % 16 == 0;
+  c->w = ws_view(p, workspace);
+  return PGG_OK;
+}
+
+pgg_status enqueue_fwd(const Call& c, const void* x, const void* weight,
+                       const int64_t* expanded_row_idx, const int64_t* group_list, float* y,
+                       hipStream_t stream) {
+  const Plan& p = c.plan;
+  hipError_t e = enqueue_prep(p, expanded_row_idx, group_list, c.w, stream);
+  if (e == hipSuccess) {
+    TimedLaunch t(forward_kernel_name(p), stream);
+    e = launch_forward(p, x, weight, y, c.aligned, c.w, stream);
+  }
+  return e == hipSuccess ? PGG_OK : PGG_ERR_HIP;
+}
+
+void fill_plan(const Plan& p, pgg_plan* out) {
+  out->regime = p.regime;
+  out->block_m = p.bm;
+  out->block_n = p.bn;
+  out->tiles_per_chunk = p.tc;
+  out->max_tiles = p.max_tiles;
+  out->max_chunks = p.max_chunks;
+  out->ring_rows = p.ring_rows;
+  out->fused_prep = p.fused_prep ? 1 : 0;
+  out->ring_bytes = p.ring_bytes;
+  out->table_bytes = p.table_bytes;
+  out->workspace_bytes = p.total;
 }
 
 }  // namespace
@@ -152,17 +208,7 @@ pgg_status pgg_moe_dx_plan(const pgg_moe_dx_desc* desc, pgg_plan* out) {
   Plan p;
   const pgg_status st = make_plan(desc, &p);
   if (st != PGG_OK) return st;
-  out->regime = p.regime;
-  out->block_m = p.bm;
-  out->block_n = p.bn;
-  out->tiles_per_chunk = p.tc;
-  out->max_tiles = p.max_tiles;
-  out->max_chunks = p.max_chunks;
-  out->ring_rows = p.ring_rows;
-  out->fused_prep = p.fused_prep ? 1 : 0;
-  out->ring_bytes = p.ring_bytes;
-  out->table_bytes = p.table_bytes;
-  out->workspace_bytes = p.total;
+  fill_plan(p, out);
   return PGG_OK;
 }
 
@@ -222,6 +268,63 @@ pgg_status pgg_moe_dx_kernel_time(const pgg_moe_dx_desc* desc, const void* grad_
   }
   *avg_ms = double(ms) / (double(repeats) * double(p.max_chunks));
   if (launches_per_call) *launches_per_call = p.max_chunks;
+  return PGG_OK;
+}
+
+pgg_status pgg_moe_fwd_workspace_size(const pgg_moe_fwd_desc* desc, size_t* bytes) {
+  if (!bytes) return PGG_ERR_INVALID_ARG;
+  Plan p;
+  const pgg_status st = make_fwd_plan(desc, &p);
+  if (st != PGG_OK) return st;
+  *bytes = p.total;
+  return PGG_OK;
+}
+
+pgg_status pgg_moe_fwd_plan(const pgg_moe_fwd_desc* desc, pgg_plan* out) {
+  if (!out) return PGG_ERR_INVALID_ARG;
+  Plan p;
+  const pgg_status st = make_fwd_plan(desc, &p);
+  if (st != PGG_OK) return st;
+  fill_plan(p, out);
+  return PGG_OK;
+}
+
+pgg_status pgg_moe_fwd(const pgg_moe_fwd_desc* desc, const void* x, const void* weight,
+                       const int64_t* expanded_row_idx, const int64_t* group_list, float* y,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  Call c;
+  const pgg_status st = check_fwd(desc, x, weight, expanded_row_idx, group_list, y, workspace,
+                                  workspace_bytes, &c);
+  if (st != PGG_OK) return st;
+  return enqueue_fwd(c, x, weight, expanded_row_idx, group_list, y, stream);
+}
+
+pgg_status pgg_moe_fwd_kernel_time(const pgg_moe_fwd_desc* desc, const void* x, const void* weight,
+                                   const int64_t* expanded_row_idx, const int64_t* group_list,
+                                   float* y, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream, int32_t repeats, double* avg_ms) {
+  if (repeats <= 0 || !avg_ms) return PGG_ERR_INVALID_ARG;
+  Call c;
+  pgg_status st = check_fwd(desc, x, weight, expanded_row_idx, group_list, y, workspace,
+                            workspace_bytes, &c);
+  if (st != PGG_OK) return st;
+  st = enqueue_fwd(c, x, weight, expanded_row_idx, group_list, y, stream);
+  if (st != PGG_OK) return st;
+  hipEvent_t ev[2] = {nullptr, nullptr};
+  for (auto& e : ev)
+    if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) st = PGG_ERR_HIP;
+  hipError_t e = st == PGG_OK ? hipEventRecord(ev[0], stream) : hipErrorUnknown;
+  for (int32_t r = 0; r < repeats && e == hipSuccess; ++r)
+    e = launch_forward(c.plan, x, weight, y, c.aligned, c.w, stream);
+  if (e == hipSuccess) e = hipEventRecord(ev[1], stream);
+  if (e == hipSuccess) e = hipEventSynchronize(ev[1]);
+  float ms = 0.0f;
+  if (e == hipSuccess) e = hipEventElapsedTime(&ms, ev[0], ev[1]);
+  for (auto& x_ev : ev)
+    if (x_ev) (void)hipEventDestroy(x_ev);
+  if (st != PGG_OK) return st;
+  if (e != hipSuccess) return PGG_ERR_HIP;
+  *avg_ms = double(ms) / double(repeats);
   return PGG_OK;
 }
 

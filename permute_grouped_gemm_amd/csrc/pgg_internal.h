@@ -44,7 +44,9 @@ constexpr size_t kRegionAlign = 512;
 constexpr size_t kWorkspaceAlign = 256;
 
 struct Plan {
-  // problem
+  // problem: N is the reduction length and K the number of output columns
+  // (the backward's N and K; a forward plan stores the forward's K in N and
+  // its N in K)
   int64_t M, N, G, K, batch, topk;
   int32_t row_idx_type;
   int32_t dtype;
@@ -64,6 +66,8 @@ struct Plan {
 
 // Fills *plan from a descriptor; returns PGG_OK or the rejection status.
 pgg_status make_plan(const pgg_moe_dx_desc* desc, Plan* plan);
+// The forward's plan: one chunk holding every m-tile, no ring.
+pgg_status make_fwd_plan(const pgg_moe_fwd_desc* desc, Plan* plan);
 
 // Views of the workspace regions.
 struct WsView {
@@ -121,5 +125,11 @@ hipError_t launch_consume(const Plan& p, int chunk, const WsView& w, float* grad
                           hipStream_t s);
 
 const char* produce_kernel_name(const Plan& p);
+
+// Forward grouped matmul with the permute gathered into the A operand:
+// y[i, :] = x[ori[i] / topK, :] · W[g(i)] for every m-tile of the plan.
+hipError_t launch_forward(const Plan& p, const void* x, const void* weight, float* y, bool aligned,
+                          const WsView& w, hipStream_t s);
+const char* forward_kernel_name(const Plan& p);
 
 }  // namespace pgg

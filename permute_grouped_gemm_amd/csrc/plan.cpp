@@ -109,4 +109,63 @@ pgg_status make_plan(const pgg_moe_dx_desc* d, Plan* p) {
   return PGG_OK;
 }
 
+pgg_status make_fwd_plan(const pgg_moe_fwd_desc* d, Plan* p) {
+  if (!d || !p) return PGG_ERR_INVALID_ARG;
+  const int64_t batch = d->x_rows, K = d->x_cols;
+  const int64_t G = d->weight_groups, N = d->weight_cols;
+  if (d->reserved != 0) return PGG_ERR_INVALID_ARG;
+  if (d->topk <= 0 || d->batch <= 0 || batch != d->batch) return PGG_ERR_INVALID_ARG;
+  if (d->row_idx_type != 0 && d->row_idx_type != 1) return PGG_ERR_INVALID_ARG;
+  if (d->x_dtype != d->weight_dtype) return PGG_ERR_INVALID_ARG;
+  if (d->x_dtype < PGG_F32 || d->x_dtype > PGG_BF16) return PGG_ERR_INVALID_ARG;
+  if (K != d->weight_rows) return PGG_ERR_INVALID_ARG;
+  if (d->group_list_len != G) return PGG_ERR_INVALID_ARG;
+  if (G <= 0 || K <= 0 || N <= 0) return PGG_ERR_INVALID_ARG;
+  if (d->topk > INT64_MAX / d->batch) return PGG_ERR_INVALID_ARG;
+  const int64_t M = d->batch * d->topk;
+  if (d->idx_len != M) return PGG_ERR_INVALID_ARG;
+  if (M >= (int64_t(1) << 31) - 1) return PGG_ERR_UNSUPPORTED;
+  if (G >= (int64_t(1) << 30) || K >= (int64_t(1) << 31) || N >= (int64_t(1) << 31))
+    return PGG_ERR_UNSUPPORTED;
+
+  Plan q{};
+  q.M = M; q.N = K; q.G = G; q.K = N; q.batch = d->batch; q.topk = d->topk;
+  q.row_idx_type = d->row_idx_type;
+  q.dtype = d->x_dtype;
+  if (q.dtype == PGG_F32) {
+    q.regime = kF32;
+    q.bm = 128; q.bn = 128;
+  } else if (M <= 64 * G) {
+    q.regime = kStream;   // few rows per expert: 32-row m-tiles
+    q.bm = 32; q.bn = 256;
+  } else {
+    q.regime = kLarge;
+    q.bm = 256; q.bn = 256;
+  }
+  const int64_t max_tiles = (M + q.bm - 1) / q.bm + G;
+  const int64_t col_tiles = (N + q.bn - 1) / q.bn;
+  // the launch grid covers max_tiles x col_tiles workgroups
+  if (max_tiles * col_tiles >= (int64_t(1) << 31) - 8 * 32) return PGG_ERR_UNSUPPORTED;
+  q.max_tiles = static_cast<int32_t>(max_tiles);
+  q.tc = q.max_tiles;
+  q.max_chunks = 1;
+  q.ring_rows = 0;
+  q.n_col_tiles = static_cast<int32_t>(col_tiles);
+  q.fused_prep = M <= 16384;
+
+  size_t off = 0;
+  q.off_header = off;   off = align_up(off + sizeof(WsHeader), kRegionAlign);
+  q.off_offsets = off;  off = align_up(off + sizeof(int64_t) * size_t(G + 1), kRegionAlign);
+  q.off_tiles = off;    off = align_up(off + sizeof(MTile) * size_t(q.max_tiles), kRegionAlign);
+  q.off_chunks = off;   off = align_up(off + sizeof(int32_t) * size_t(q.max_chunks + 1), kRegionAlign);
+  q.off_inv = off;      off = align_up(off + sizeof(int32_t) * size_t(M), kRegionAlign);
+  q.off_ori = off;      off = align_up(off + sizeof(int32_t) * size_t(M), kRegionAlign);
+  q.table_bytes = off;
+  q.off_ring = off;
+  q.ring_bytes = 0;
+  q.total = off;
+  *p = q;
+  return PGG_OK;
+}
+
 }  // namespace pgg

@@ -104,3 +104,81 @@ def test_timing_hook_guards():
     assert L.pgg_timing_begin(0) == pgg.ERR_INVALID_ARG
     n = ctypes.c_int32()
     assert L.pgg_timing_end(None, 0, ctypes.byref(n)) == pgg.ERR_INVALID_ARG
+
+
+# ---------------------------------------------------------------- forward
+
+def fdesc(batch=64, K=96, G=4, N=64, topk=2, L=None, Gl=None, rit=0, dx=F32, dw=None, Kw=None,
+          xrows=None):
+    return pgg.make_fwd_desc((batch if xrows is None else xrows, K), (G, K if Kw is None else Kw, N),
+                             batch * topk if L is None else L, G if Gl is None else Gl, batch, topk,
+                             rit, dx, dx if dw is None else dw)
+
+
+def fwd_status_of_size(d):
+    n = ctypes.c_size_t()
+    return pgg.lib().pgg_moe_fwd_workspace_size(ctypes.byref(d), ctypes.byref(n)), n.value
+
+
+@pytest.mark.parametrize("bad", [
+    dict(Kw=97), dict(Gl=3), dict(L=127), dict(L=129), dict(xrows=63), dict(topk=0),
+    dict(batch=0, xrows=0), dict(rit=2), dict(dw=F16), dict(dx=3, dw=3), dict(G=0, Gl=0),
+    dict(N=0), dict(K=0, Kw=0),
+])
+def test_forward_invalid_descriptors_rejected(bad):
+    st, _ = fwd_status_of_size(fdesc(**bad))
+    assert st == pgg.ERR_INVALID_ARG
+
+
+def test_forward_reserved_and_size_limits():
+    d = fdesc()
+    d.reserved = 1
+    assert fwd_status_of_size(d)[0] == pgg.ERR_INVALID_ARG
+    M = 1 << 31
+    assert fwd_status_of_size(fdesc(batch=M // 2, topk=2))[0] == pgg.ERR_UNSUPPORTED
+
+
+def test_forward_workspace_holds_only_tables():
+    # no fp32 buffer: the workspace is O(M + G) integers whatever K and N
+    sizes = []
+    for K, N in ((128, 256), (7168, 2048), (7168, 4096)):
+        st, n = fwd_status_of_size(fdesc(batch=13824, topk=8, G=60, K=K, N=N, dx=F16))
+        assert st == pgg.OK
+        sizes.append(n)
+    assert len(set(sizes)) == 1
+    M, G = 13824 * 8, 60
+    assert sizes[0] <= 2 * 4 * M + 8 * (G + 1) + 16 * (M // 256 + G + 1) + 4 * 512
+
+
+def test_forward_plan_regimes():
+    def plan(**kw):
+        d = fdesc(**kw)
+        p = pgg.Plan()
+        assert pgg.lib().pgg_moe_fwd_plan(ctypes.byref(d), ctypes.byref(p)) == pgg.OK
+        return p.as_dict()
+    assert plan(dx=F32)["regime"] == 2
+    dec = plan(batch=16, topk=8, G=16, K=7168, N=4096, dx=BF16)
+    assert dec["regime"] == 1 and dec["block_m"] == 32 and dec["max_chunks"] == 1
+    big = plan(batch=13824, topk=8, G=60, K=7168, N=2048, dx=F16)
+    assert big["regime"] == 0 and big["block_m"] == 256 and big["ring_bytes"] == 0
+    assert big["max_tiles"] == -(-110592 // 256) + 60 == big["tiles_per_chunk"]
+
+
+def test_forward_execute_rejects_before_any_launch():
+    L = pgg.lib()
+    d = fdesc()
+    n = ctypes.c_size_t()
+    assert L.pgg_moe_fwd_workspace_size(ctypes.byref(d), ctypes.byref(n)) == pgg.OK
+    need = n.value
+    fake = 0x100000  # never dereferenced: every case below fails validation first
+    args = [fake, fake, fake, fake, fake]
+    bad = fdesc(topk=0)
+    assert L.pgg_moe_fwd(ctypes.byref(bad), *args, fake, need, None) == pgg.ERR_INVALID_ARG
+    assert L.pgg_moe_fwd(ctypes.byref(d), None, fake, fake, fake, fake, fake, need, None) == pgg.ERR_INVALID_ARG
+    assert L.pgg_moe_fwd(ctypes.byref(d), *args, None, need, None) == pgg.ERR_INVALID_ARG
+    assert L.pgg_moe_fwd(ctypes.byref(d), *args, fake, need - 1, None) == pgg.ERR_WORKSPACE_TOO_SMALL
+    assert L.pgg_moe_fwd(ctypes.byref(d), *args, fake + 8, need, None) == pgg.ERR_MISALIGNED
+    # y not 4-byte aligned
+    assert L.pgg_moe_fwd(ctypes.byref(d), fake, fake, fake, fake, fake + 2, fake, need, None) == pgg.ERR_MISALIGNED
+    avg = ctypes.c_double()
+    assert L.pgg_moe_fwd_kernel_time(ctypes.byref(d), *args, fake, need, None, 0, ctypes.byref(avg)) == pgg.ERR_INVALID_ARG
