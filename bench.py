@@ -18,6 +18,10 @@ launches of that kernel alone (pgg_moe_dx_kernel_time, on the stream the
 calls use); an event pair around each launch inside the calls would add the
 launch's dispatch latency to every measurement.  The CPU baseline is the oracle on a bounded sample of the same
 workload, timed on this host.
+
+Each workload also reports the layer's forward (Permute + GroupedMatmul,
+pgg_moe_fwd) on its routing and weights under "forward" (--no-forward skips
+it); the headline value stays the fused backward's.
 """
 from __future__ import annotations
 
@@ -78,7 +82,81 @@ def algorithmic(case):
     return flops, bytes_, producer_bytes
 
 
-def measure(name, steps, warmup, cpu_baseline, log):
+def algorithmic_forward(case):
+    """Algorithmic flops and bytes of one forward call: x (each token row once)
+    + weights of non-empty experts + routing index + group_list + y written
+    once (fp32); flops = 2*M*K*N."""
+    import numpy as np
+    s = {"f32": 4, "f16": 2, "bf16": 2}[case.dtype]
+    g_ne = int(np.count_nonzero(case.group_list))
+    flops = 2.0 * case.M * case.N * case.K
+    kernel_bytes = case.batch * case.K * s + g_ne * case.K * case.N * s + 4 * case.M * case.N
+    return flops, kernel_bytes + 8 * case.M + 8 * case.G, kernel_bytes
+
+
+def measure_forward(case, w, eri, gl, steps, log):
+    """The layer's forward (Permute + GroupedMatmul) on the workload's own
+    routing and weights, with seeded activations x [batch, K]."""
+    import numpy as np
+    import torch
+
+    import permute_grouped_gemm_amd as pgg
+    import synth
+
+    dev = w.device
+    x = synth.forward_input(case)
+    if case.dtype == "bf16":
+        xt = torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+    else:
+        xt = torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+    plan = pgg.fwd_plan(xt, w, eri, gl, case.topk, case.row_idx_type)
+    ws = torch.empty(plan["workspace_bytes"], dtype=torch.uint8, device=dev)
+    y = torch.empty((case.M, case.N), dtype=torch.float32, device=dev)
+
+    def step():
+        pgg.moe_fwd(xt, w, eri, gl, case.topk, case.row_idx_type, out=y, workspace=ws)
+
+    t_settle = time.time()
+    while time.time() - t_settle < SETTLE_S:
+        for _ in range(4):
+            step()
+        torch.cuda.synchronize()
+    code, detail = pgg.read_device_error(ws)
+    if code != 0:
+        raise RuntimeError(f"forward device error {code} ({detail})")
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        step()
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    k_ms = pgg.fwd_kernel_time(xt, w, eri, gl, case.topk, case.row_idx_type, repeats=steps, out=y,
+                               workspace=ws)
+    flops, bytes_, kernel_bytes = algorithmic_forward(case)
+    kname = {0: "forward_large", 1: "forward_stream", 2: "forward_f32"}[plan["regime"]]
+    if plan["regime"] == 1:
+        achieved = kernel_bytes / (k_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS}
+    else:
+        peak = PEAK_TFLOPS[case.dtype]
+        achieved = flops / (k_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                "frac": achieved / peak}
+    roof.update({"kernel": kname, "avg_launch_us": k_ms * 1e3, "launches_per_step": 1})
+    log(f"[bench] {case.name} forward: {ms * 1e3:.1f} us/call, {kname} {k_ms * 1e3:.1f} us "
+        f"(back to back), {flops / (ms * 1e-3) / 1e12:.1f} TFLOP/s, {bytes_ / (ms * 1e-3) / 1e9:.0f} GB/s")
+    return {"ms_per_call": ms, "tflops": flops / (ms * 1e-3) / 1e12,
+            "gbs": bytes_ / (ms * 1e-3) / 1e9, "frac_bf16_peak": flops / (ms * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"],
+            "frac_hbm": bytes_ / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "roofline": roof,
+            "algorithmic_bytes": bytes_, "flops": flops, "plan": plan,
+            "what": "y[i,n] = sum_k x[p(i)//topK, k] W[g(i),k,n] on the workload's routing and "
+                    "weights, x ~ N(0,1) seeded; time covers the index preparation and the kernel"}
+
+
+def measure(name, steps, warmup, cpu_baseline, log, forward=True):
     import numpy as np
     import torch
 
@@ -219,6 +297,8 @@ def measure(name, steps, warmup, cpu_baseline, log):
                    "K": case.K, "N": case.N, "row_idx_type": case.row_idx_type,
                    "algorithmic_bytes": bytes_, "flops": flops},
     }
+    if forward:
+        res["forward"] = measure_forward(case, w, eri, gl, steps, log)
     if cpu_baseline:
         res["cpu_baseline"] = oracle_baseline(case, unit, log)
     return res
@@ -326,6 +406,8 @@ def main():
     ap.add_argument("--workload", default="decode_bf16")
     ap.add_argument("--no-large", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-forward", action="store_true",
+                    help="skip the forward (Permute + GroupedMatmul) measurement")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -344,7 +426,8 @@ def main():
     if args.calibrate_copy:
         calibrate_copy(log)
         return 0
-    primary = measure(args.workload, args.steps, args.warmup, not args.no_cpu_baseline, log)
+    primary = measure(args.workload, args.steps, args.warmup, not args.no_cpu_baseline, log,
+                      forward=not args.no_forward)
     line = {
         "metric": METRIC,
         "value": primary["value"], "unit": primary["unit"], "n_gpus": 1,
@@ -362,9 +445,11 @@ def main():
                                               "kernels_event_bracketed_ms_per_step",
                                               "workspace_bytes", "ring_bytes",
                                               "d_expanded_x_fp32_bytes", "plan")}
+    if "forward" in primary:
+        line["forward"] = primary["forward"]
     if not args.no_large and args.workload != "large_f16":
         large = measure("large_f16", max(5, args.steps // 2), args.warmup,
-                        not args.no_cpu_baseline, log)
+                        not args.no_cpu_baseline, log, forward=not args.no_forward)
         line["large"] = {k: large[k] for k in ("value", "unit", "ms_per_step", "tflops", "gbs",
                                                "smi_sclk_after_timing",
                                                "frac_bf16_peak", "roofline", "kernels_ms_per_step",
@@ -373,6 +458,8 @@ def main():
                                                "d_expanded_x_fp32_bytes", "config", "dtype")}
         if "cpu_baseline" in large:
             line["large"]["cpu_baseline"] = large["cpu_baseline"]
+        if "forward" in large:
+            line["large"]["forward"] = large["forward"]
     print(json.dumps(line), flush=True)
     return 0
 
