@@ -30,6 +30,9 @@
 // s ^ swz(k), so the rows one read instruction touches land on different
 // banks (4 consecutive rows for the transposed read; rows k and k+4 for fp32).
 //
+// Aligned 16-bit rows with many rows per expert take the direct-to-LDS tile
+// of fwd_large.hip instead.
+//
 // Row tails (an expert's last tile), column tails (N not a multiple of BN)
 // and reduction tails (K not a multiple of BK) are zero-filled on load and
 // masked on store.  ALIGNED=false handles rows that are not 16-byte aligned
@@ -273,6 +276,7 @@ hipError_t launch_forward(const Plan& p, const void* x, const void* weight, floa
     if (p.dtype == PGG_BF16) return launch_typed<TBf16, 32, 256, 1, 4>(p, a, aligned, s);
     return launch_typed<TF16, 32, 256, 1, 4>(p, a, aligned, s);
   }
+  if (aligned) return launch_forward_large(p, x, weight, y, w, s);
   if (p.dtype == PGG_BF16) return launch_typed<TBf16, 256, 256, 2, 2>(p, a, aligned, s);
   return launch_typed<TF16, 256, 256, 2, 2>(p, a, aligned, s);
 }

@@ -131,5 +131,8 @@ const char* produce_kernel_name(const Plan& p);
 hipError_t launch_forward(const Plan& p, const void* x, const void* weight, float* y, bool aligned,
                           const WsView& w, hipStream_t s);
 const char* forward_kernel_name(const Plan& p);
+// 256x256 direct-to-LDS forward tile (16-bit types, 16-byte aligned rows).
+hipError_t launch_forward_large(const Plan& p, const void* x, const void* weight, float* y,
+                                const WsView& w, hipStream_t s);
 
 }  // namespace pgg
