@@ -243,7 +243,9 @@ typedef struct {
 } pgg_moe_fwd_desc;
 
 /* Workspace size of the forward (host only; shapes only): O(M + G) integer
- * index and tile tables, no fp32 buffer. */
+ * index and tile tables, plus -- for few rows per expert (M <= 64 G, 16-bit
+ * types), when the reduction is split over workgroups -- fp32 partials of y,
+ * ksplit x M x N floats with ksplit <= 8. */
 pgg_status pgg_moe_fwd_workspace_size(const pgg_moe_fwd_desc* desc, size_t* bytes);
 
 /*
@@ -267,7 +269,8 @@ pgg_status pgg_moe_fwd(const pgg_moe_fwd_desc* desc, const void* x, const void* 
 
 /* Plan of the forward (host only): regime 0 = 256x256 tiles, 1 = 32-row
  * m-tiles for few rows per expert, 2 = fp32; tiles_per_chunk = max_tiles,
- * max_chunks = 1, ring fields 0. */
+ * max_chunks = 1; ring_rows / ring_bytes describe the split partials
+ * (ksplit x M rows of N floats; 0 when the reduction is not split). */
 pgg_status pgg_moe_fwd_plan(const pgg_moe_fwd_desc* desc, pgg_plan* plan);
 
 /*

@@ -173,6 +173,10 @@ pgg_status enqueue_fwd(const Call& c, const void* x, const void* weight,
     TimedLaunch t(forward_kernel_name(p), stream);
     e = launch_forward(p, x, weight, y, c.aligned, c.w, stream);
   }
+  if (e == hipSuccess && p.ksplit > 1) {
+    TimedLaunch t("forward_reduce", stream);
+    e = launch_forward_reduce(p, c.w, y, stream);
+  }
   return e == hipSuccess ? PGG_OK : PGG_ERR_HIP;
 }
 

@@ -11,7 +11,11 @@
 // Workgroup = one output tile (BM expanded rows of one expert x BN output
 // columns), waves laid out WM x WN, each owning (BM/WM) x (BN/WN) of 32x32
 // MFMA accumulators.  The reduction over k runs in stages of BK elements,
-// double-buffered in LDS with a register prefetch of the next stage.
+// double-buffered in LDS with a register prefetch of the next stage.  With
+// few rows per expert the reduction may be split (blockIdx.y = split, kspan
+// elements each, a multiple of BK): each split writes an fp32 partial tile
+// to the workspace and fwd_reduce_kernel adds the splits in split order, so
+// the result does not depend on timing.
 //
 // Operand layouts.  A gathered x row is contiguous along k, the reduction,
 // which is what an MFMA operand wants (every lane takes a run of consecutive
@@ -37,6 +41,8 @@
 // and reduction tails (K not a multiple of BK) are zero-filled on load and
 // masked on store.  ALIGNED=false handles rows that are not 16-byte aligned
 // with element loads.
+#include <algorithm>
+
 #include "pgg_device.h"
 
 namespace pgg {
@@ -52,8 +58,9 @@ struct FwdArgs {
   const WsHeader* hdr;
   const MTile* tiles;
   const int32_t* ori;       // expanded row -> original position
-  float* y;                 // [M, C]
+  float* y;                 // [M, C], or the split partials [ksplit, M, C]
   int64_t R, C, topk;       // reduction length (K), output columns (N), topK
+  int64_t M, kspan;         // expanded rows; reduction elements per split (blockIdx.y)
   int32_t n_slots, n_col_tiles;
 };
 
@@ -100,10 +107,14 @@ void fwd_kernel(FwdArgs a) {
   const int rows = tile.rows;
   const int64_t col0 = static_cast<int64_t>(ct) * BN;
   const int cols = static_cast<int>(min<int64_t>(BN, a.C - col0));
-  const int64_t R = a.R, C = a.C;
+  const int64_t C = a.C;
+  // reduction range of this workgroup's split: [kbeg, R)
+  const int64_t kbeg = static_cast<int64_t>(blockIdx.y) * a.kspan;
+  const int64_t R = min<int64_t>(a.R, kbeg + a.kspan);
+  const int64_t RX = a.R;     // x row length
 
   const E* __restrict__ X = static_cast<const E*>(a.X);
-  const E* __restrict__ Wg = static_cast<const E*>(a.W) + static_cast<int64_t>(tile.g) * R * C;
+  const E* __restrict__ Wg = static_cast<const E*>(a.W) + static_cast<int64_t>(tile.g) * RX * C;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -120,12 +131,12 @@ void fwd_kernel(FwdArgs a) {
   for (int s = 0; s < A_PER_T; ++s) {
     const int r = (tid + s * NT) / kChunks;
     const int64_t tok = r < rows ? a.ori[tile.row0 + r] / a.topk : 0;
-    arow[s] = X + tok * R;
+    arow[s] = X + tok * RX;
   }
 
   u32x4_t ra[A_PER_T], rb[B_PER_T];
   auto load_stage = [&](int kt) {
-    const int64_t k0 = static_cast<int64_t>(kt) * BK;
+    const int64_t k0 = kbeg + static_cast<int64_t>(kt) * BK;
 #pragma unroll
     for (int s = 0; s < A_PER_T; ++s) {
       const int q = tid + s * NT;
@@ -215,7 +226,7 @@ void fwd_kernel(FwdArgs a) {
     }
   };
 
-  const int nk = static_cast<int>((R + BK - 1) / BK);
+  const int nk = static_cast<int>((R - kbeg + BK - 1) / BK);
   load_stage(0);
   store_stage(0);
   __syncthreads();
@@ -229,7 +240,8 @@ void fwd_kernel(FwdArgs a) {
 
   // Epilogue: accumulator v of lane (lr, lh) is row 8*(v/4) + 4*lh + v%4,
   // column lr of its 32x32 block.
-  float* __restrict__ out = a.y + static_cast<int64_t>(tile.row0) * C + col0;
+  float* __restrict__ out =
+      a.y + (static_cast<int64_t>(blockIdx.y) * a.M + tile.row0) * C + col0;
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -248,11 +260,24 @@ hipError_t launch_typed(const Plan& p, const FwdArgs& a, bool aligned, hipStream
   unsigned tiles = static_cast<unsigned>(a.n_slots) * static_cast<unsigned>(a.n_col_tiles);
   tiles = (tiles + 8 * 32 - 1) / (8 * 32) * (8 * 32);   // whole raster rounds
   if (tiles == 0) return hipSuccess;
+  const dim3 grid(tiles, static_cast<unsigned>(p.ksplit));
   if (aligned)
-    hipLaunchKernelGGL((fwd_kernel<T, BM, BN, WM, WN, true>), dim3(tiles), dim3(WM * WN * 64), 0, s, a);
+    hipLaunchKernelGGL((fwd_kernel<T, BM, BN, WM, WN, true>), grid, dim3(WM * WN * 64), 0, s, a);
   else
-    hipLaunchKernelGGL((fwd_kernel<T, BM, BN, WM, WN, false>), dim3(tiles), dim3(WM * WN * 64), 0, s, a);
+    hipLaunchKernelGGL((fwd_kernel<T, BM, BN, WM, WN, false>), grid, dim3(WM * WN * 64), 0, s, a);
   return hipGetLastError();
+}
+
+// y[e] = part[0][e] + part[1][e] + ... in split order (e over all M x C).
+__global__ __launch_bounds__(256) void fwd_reduce_kernel(const WsHeader* hdr, const float* part,
+                                                         float* y, int64_t n, int32_t ksplit) {
+  if (hdr->err != kNoError) return;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < n; e += stride) {
+    float acc = part[e];
+    for (int32_t s = 1; s < ksplit; ++s) acc += part[static_cast<int64_t>(s) * n + e];
+    y[e] = acc;
+  }
 }
 
 }  // namespace
@@ -265,10 +290,12 @@ hipError_t launch_forward(const Plan& p, const void* x, const void* weight, floa
   a.hdr = w.hdr;
   a.tiles = w.tiles;
   a.ori = w.ori;
-  a.y = y;
+  a.y = p.ksplit > 1 ? w.ring : y;   // split partials go to the workspace
   a.R = p.N;            // the plan keeps the reduction length in N
   a.C = p.K;            // and the output columns in K
   a.topk = p.topk;
+  a.M = p.M;
+  a.kspan = p.kspan;
   a.n_slots = p.max_tiles;
   a.n_col_tiles = p.n_col_tiles;
   if (p.dtype == PGG_F32) return launch_typed<TF32, 128, 128, 2, 2>(p, a, aligned, s);
@@ -279,6 +306,14 @@ hipError_t launch_forward(const Plan& p, const void* x, const void* weight, floa
   if (aligned) return launch_forward_large(p, x, weight, y, w, s);
   if (p.dtype == PGG_BF16) return launch_typed<TBf16, 256, 256, 2, 2>(p, a, aligned, s);
   return launch_typed<TF16, 256, 256, 2, 2>(p, a, aligned, s);
+}
+
+hipError_t launch_forward_reduce(const Plan& p, const WsView& w, float* y, hipStream_t s) {
+  const int64_t n = p.M * p.K;
+  const int64_t blocks = std::min<int64_t>((n + 255) / 256, 2048);
+  hipLaunchKernelGGL(fwd_reduce_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, w.hdr,
+                     w.ring, y, n, p.ksplit);
+  return hipGetLastError();
 }
 
 const char* forward_kernel_name(const Plan& p) {

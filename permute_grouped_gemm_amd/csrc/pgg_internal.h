@@ -58,6 +58,8 @@ struct Plan {
   int32_t max_chunks;  // ceil(max_tiles / tc)
   int32_t ring_rows;   // tc * bm
   int32_t n_col_tiles; // ceil(K / bn)
+  int32_t ksplit;      // forward, few rows per expert: reduction splits (partials in the ring region)
+  int32_t kspan;       // reduction elements per split
   bool fused_prep;
   // layout (byte offsets into the workspace)
   size_t off_header, off_offsets, off_tiles, off_chunks, off_inv, off_ori, off_ring, total;
@@ -132,6 +134,8 @@ hipError_t launch_forward(const Plan& p, const void* x, const void* weight, floa
                           const WsView& w, hipStream_t s);
 const char* forward_kernel_name(const Plan& p);
 // 256x256 direct-to-LDS forward tile (16-bit types, 16-byte aligned rows).
+// Sum of the forward's reduction splits, in split order, into y.
+hipError_t launch_forward_reduce(const Plan& p, const WsView& w, float* y, hipStream_t s);
 hipError_t launch_forward_large(const Plan& p, const void* x, const void* weight, float* y,
                                 const WsView& w, hipStream_t s);
 

@@ -92,6 +92,8 @@ pgg_status make_plan(const pgg_moe_dx_desc* d, Plan* p) {
   q.ring_rows = q.tc * q.bm;
   q.n_col_tiles = static_cast<int32_t>((K + q.bn - 1) / q.bn);
   q.fused_prep = M <= 16384;
+  q.ksplit = 1;
+  q.kspan = static_cast<int32_t>(N);
 
   size_t off = 0;
   q.off_header = off;   off = align_up(off + sizeof(WsHeader), kRegionAlign);
@@ -152,6 +154,25 @@ pgg_status make_fwd_plan(const pgg_moe_fwd_desc* d, Plan* p) {
   q.ring_rows = 0;
   q.n_col_tiles = static_cast<int32_t>(col_tiles);
   q.fused_prep = M <= 16384;
+  // Few rows per expert: each tile streams its expert's weight columns over
+  // the whole reduction.  When the tiles alone would leave the GPU short of
+  // workgroups (at most max_tiles x col_tiles have work), the reduction is
+  // split so about 1024 workgroups stream at once; each split writes an fp32
+  // partial of y and a reduction kernel adds them in split order.
+  q.ksplit = 1;
+  q.kspan = static_cast<int32_t>(K);
+  if (q.regime == kStream) {
+    constexpr int64_t kStage = 64, kMinSpan = 512, kTarget = 1024;
+    const int64_t units = max_tiles * col_tiles;
+    int64_t split = (kTarget + units - 1) / units;
+    split = std::min<int64_t>(split, std::max<int64_t>(1, K / kMinSpan));
+    split = std::max<int64_t>(1, std::min<int64_t>(split, 8));
+    int64_t span = (K + split - 1) / split;
+    span = (span + kStage - 1) / kStage * kStage;
+    split = (K + span - 1) / span;
+    q.ksplit = static_cast<int32_t>(split);
+    q.kspan = static_cast<int32_t>(span);
+  }
 
   size_t off = 0;
   q.off_header = off;   off = align_up(off + sizeof(WsHeader), kRegionAlign);
@@ -162,7 +183,9 @@ pgg_status make_fwd_plan(const pgg_moe_fwd_desc* d, Plan* p) {
   q.off_ori = off;      off = align_up(off + sizeof(int32_t) * size_t(M), kRegionAlign);
   q.table_bytes = off;
   q.off_ring = off;
-  q.ring_bytes = 0;
+  q.ring_bytes = q.ksplit > 1 ? size_t(q.ksplit) * size_t(M) * size_t(N) * sizeof(float) : 0;
+  q.ring_rows = q.ksplit > 1 ? static_cast<int32_t>(q.ksplit * M) : 0;
+  off = align_up(off + q.ring_bytes, kRegionAlign);
   q.total = off;
   *p = q;
   return PGG_OK;

@@ -56,6 +56,8 @@ FWD_SHAPES = [
     dict(batch=32, topk=8, G=16, K=520, N=264, routing="heavy", empty=(3,), heavy=5,
          heavy_rows=100),                                         # one expert with 4 m-tiles
     dict(batch=300, topk=2, G=2, K=64, N=256, row_idx_type=1),    # 256x256 tiles, scatter-form index
+    dict(batch=20, topk=4, G=8, K=3000, N=520),                   # reduction split 5 ways, last one a tail
+    dict(batch=20, topk=4, G=8, K=3001, N=520),                   # the same with unaligned x rows
 ]
 
 
@@ -64,6 +66,8 @@ FWD_SHAPES = [
 def test_forward_integer_inputs_bit_exact(orc, kw, dtype):
     case = synth.make_case(dtype=dtype, seed=900, integer=True, **kw)
     x = synth.forward_input(case, integer=True)
+    print(f"[fwd] {kw} {dtype} plan {pgg.fwd_plan(*upload_fwd(case, x), case.topk, case.row_idx_type)}",
+          flush=True)
     got = run_fwd(case, x)
     want = orc.case_fwd(case, x)
     assert 4 * case.K < 2 ** 24
