@@ -398,6 +398,38 @@ def calibrate_copy(log, mib=1024, reps=5):
     print(json.dumps({"copy_bytes": n, "reps": reps}), flush=True)
 
 
+def vendor_gemm(log, reps=100):
+    """Reference point: hipBLASLt (torch.mm) on one chunk of the large fp16
+    workload as a plain dense GEMM, [9216 x 2048] x [2048 x 7168] -- the
+    producer's shape without grouping or routing -- with fp16 and fp32
+    output.  Not part of the path; printed as its own JSON line."""
+    import torch
+    torch.manual_seed(0)
+    M, R, C = 9216, 2048, 7168
+    a = torch.randn(M, R, device="cuda", dtype=torch.float16)
+    wt = torch.randn(C, R, device="cuda", dtype=torch.float16).t()
+    flops = 2.0 * M * R * C
+    res = {}
+    for name, fn in (("fp16_out", lambda: torch.mm(a, wt)),
+                     ("fp32_out", lambda: torch.mm(a, wt, out_dtype=torch.float32))):
+        t_end = time.time() + 0.2
+        while time.time() < t_end:
+            for _ in range(10):
+                fn()
+            torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / reps * 1e3
+        res[name] = {"us": us, "tflops": flops / us / 1e6}
+        log(f"[bench] vendor dense GEMM {M}x{R}x{C} {name}: {us:.1f} us, {flops / us / 1e6:.0f} TFLOP/s")
+    print(json.dumps({"vendor_dense_gemm": res, "shape": [M, R, C], "library": "torch.mm (hipBLASLt)"}),
+          flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -410,6 +442,8 @@ def main():
                     help="skip the forward (Permute + GroupedMatmul) measurement")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="only time hipBLASLt (torch.mm) on the large workload's per-chunk dense GEMM")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not supported",
@@ -425,6 +459,9 @@ def main():
         return 1
     if args.calibrate_copy:
         calibrate_copy(log)
+        return 0
+    if args.vendor_gemm:
+        vendor_gemm(log)
         return 0
     primary = measure(args.workload, args.steps, args.warmup, not args.no_cpu_baseline, log,
                       forward=not args.no_forward)
