@@ -15,7 +15,9 @@ section literally, with its indicator function, for tiny inputs.
 ``moe_fwd`` is the forward chain of the same section (MoeInitRouting =
 Permute, then GroupedMatmul): expanded row i copies token p(i) / topK of x,
 and every expert's rows are multiplied by that expert's weight slice, in
-float64, with numpy's matmul as the per-expert product.
+float64, with numpy's matmul as the per-expert product.  ``moe_dw`` is the
+weight gradient the page leaves to a separate operator (§1.2):
+expanded_x^T · d_y per expert, the same way.
 
 Parity status: every function here is pinned by the CPU tests in
 ``tests/test_oracle_*.py`` (brute force, library matmul special cases, the
@@ -258,6 +260,51 @@ def moe_fwd(x, weight, eri, group_list, batch, topk, row_idx_type, dtype, *, row
         if want_abs:
             absdot[at] = np.abs(xg) @ np.abs(wg)
     return (y, absdot) if want_abs else y
+
+
+def moe_dw(x, grad_y, eri, group_list, batch, topk, row_idx_type, dtype, *, experts=None,
+           want_abs=False):
+    """Weight gradient dW[g, k, n] = sum over expert g's expanded rows i of
+    x[p(i) // topK, k] * grad_y[i, n], in float64.
+
+    MoeInitRoutingGroupedMatmulGrad design page, §1.2 (why d_weight is left
+    to a separate operator): d_weight [G, K, N] = expanded_x^T @ d_y per
+    expert, with expanded_x = Permute(x) as in the forward formulas of
+    §数学定义和公式.  x is [batch, K], grad_y [M, N], in the storage type
+    ``dtype``.  An expert with no rows gets zeros.  ``experts`` (optional)
+    selects experts; the result has one [K, N] slice per entry.  With
+    want_abs, also returns the sums of |x|·|grad_y| over the same terms.
+    """
+    x = np.ascontiguousarray(x)
+    grad_y = np.ascontiguousarray(grad_y)
+    if x.ndim != 2 or grad_y.ndim != 2:
+        raise OracleError(ERR_SHAPE, "rank")
+    M = batch * topk
+    G = int(np.shape(group_list)[0])
+    K, N = x.shape[1], grad_y.shape[1]
+    if x.shape[0] != batch or grad_y.shape[0] != M or np.shape(eri) != (M,):
+        raise OracleError(ERR_SHAPE, "shape")
+    off = offsets(group_list, M)
+    ori, _ = index(eri, row_idx_type)
+    sel = np.arange(G) if experts is None else np.asarray(experts, dtype=np.int64)
+    dw = np.zeros((sel.size, K, N), dtype=np.float64)
+    absdot = np.zeros((sel.size, K, N), dtype=np.float64) if want_abs else None
+    for at, g in enumerate(sel):
+        r0, r1 = int(off[g]), int(off[g + 1])
+        if r1 == r0:
+            continue
+        xg = decode(x[ori[r0:r1] // topk], dtype)        # expanded_x rows of expert g
+        dyg = decode(grad_y[r0:r1], dtype)
+        dw[at] = xg.T @ dyg
+        if want_abs:
+            absdot[at] = np.abs(xg).T @ np.abs(dyg)
+    return (dw, absdot) if want_abs else dw
+
+
+def case_dw(case, x, **kw):
+    """moe_dw on a ``synth.Case`` (its grad_y and routing) and activations x."""
+    return moe_dw(x, case.grad_y, case.eri, case.group_list, case.batch, case.topk,
+                  case.row_idx_type, case.dtype, **kw)
 
 
 def case_fwd(case, x, **kw):
