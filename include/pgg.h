@@ -120,8 +120,8 @@ pgg_status pgg_moe_dx(const pgg_moe_dx_desc* desc, const void* grad_y, const voi
                       hipStream_t stream);
 
 /*
- * Read the device error word of the last pgg_moe_dx (or pgg_moe_fwd) that
- * used `workspace`.
+ * Read the device error word of the last pgg_moe_dx (or pgg_moe_fwd,
+ * pgg_moe_dw) that used `workspace`.
  * Synchronises `stream`.  *code receives a pgg_device_error; *detail its
  * detail value (may be NULL).  When several violations exist, the one with
  * the smallest (code, detail) is reported, so the report is deterministic.
@@ -285,6 +285,34 @@ pgg_status pgg_moe_fwd_kernel_time(const pgg_moe_fwd_desc* desc, const void* x, 
                                    const int64_t* expanded_row_idx, const int64_t* group_list,
                                    float* y, void* workspace, size_t workspace_bytes,
                                    hipStream_t stream, int32_t repeats, double* avg_ms);
+
+/*
+ * Weight gradient of the same layer: the operator the design page leaves
+ * d_weight to (MoeInitRoutingGroupedMatmulGrad design page, §1.2, expanded_x^T
+ * @ d_y per expert), with the permute fused into the operand load:
+ *
+ *     grad_w[g,k,n] = sum over expert g's expanded rows i of x[p(i)/topK, k] * grad_y[i, n]
+ *
+ * fp32 accumulation; grad_w is float32 [G, K, N], fully overwritten (an expert
+ * without rows gets zeros).  Each output element is reduced by one
+ * workgroup in a fixed order, so repeated calls give bit-identical results.
+ * It takes the forward's descriptor: x [x_rows = batch, x_cols = K],
+ * weight_groups / weight_rows / weight_cols = G, K, N (the shape of grad_w),
+ * expanded_row_idx and group_list as for pgg_moe_dx; grad_y is [batch*topk, N]
+ * in the same dtype (x_dtype == weight_dtype names it).
+ * Errors and workspace rules as for pgg_moe_fwd; the workspace holds only
+ * the O(M + G) index tables.
+ */
+pgg_status pgg_moe_dw_workspace_size(const pgg_moe_fwd_desc* desc, size_t* bytes);
+pgg_status pgg_moe_dw(const pgg_moe_fwd_desc* desc, const void* x, const void* grad_y,
+                      const int64_t* expanded_row_idx, const int64_t* group_list, float* grad_w,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Kernel benchmark hook of the weight gradient, as pgg_moe_fwd_kernel_time. */
+pgg_status pgg_moe_dw_kernel_time(const pgg_moe_fwd_desc* desc, const void* x, const void* grad_y,
+                                  const int64_t* expanded_row_idx, const int64_t* group_list,
+                                  float* grad_w, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream, int32_t repeats, double* avg_ms);
 
 const char* pgg_status_string(pgg_status status);
 const char* pgg_device_error_string(int32_t code);

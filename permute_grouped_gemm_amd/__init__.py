@@ -17,6 +17,11 @@ sum_n grad_y[i,n] * weight[g(i),k,n], returned as float32 [batch, K].
 is the layer's forward (the same section's forward formulas): Permute then
 GroupedMatmul, y[i,n] = sum_k x[p(i) // topK, k] * weight[g(i),k,n], float32
 [M, N] in expanded (expert-grouped) row order.
+
+    grad_w = moe_dw(x, grad_y, expanded_row_idx, group_list, topk, row_idx_type)
+
+is the weight gradient (§1.2's separate operator, expanded_x^T · d_y per
+expert), float32 [G, K, N].
 """
 from __future__ import annotations
 
@@ -30,6 +35,7 @@ import torch
 __all__ = [
     "moe_dx", "workspace_size", "plan", "read_device_error", "debug_tables", "debug_tiles",
     "moe_fwd", "fwd_workspace_size", "fwd_plan", "fwd_kernel_time",
+    "moe_dw", "dw_workspace_size", "dw_kernel_time",
     "KernelTimer", "PggError", "lib", "LIB_PATH", "HEADER_PATH",
 ]
 
@@ -116,6 +122,10 @@ def lib():
         L.pgg_moe_fwd_plan.argtypes = [PF, ctypes.POINTER(Plan)]
         L.pgg_moe_fwd_kernel_time.argtypes = [PF, vp, vp, vp, vp, vp, vp, sz, vp, i32,
                                                ctypes.POINTER(ctypes.c_double)]
+        L.pgg_moe_dw_workspace_size.argtypes = [PF, ctypes.POINTER(sz)]
+        L.pgg_moe_dw.argtypes = [PF, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.pgg_moe_dw_kernel_time.argtypes = [PF, vp, vp, vp, vp, vp, vp, sz, vp, i32,
+                                              ctypes.POINTER(ctypes.c_double)]
         L.pgg_timing_begin.argtypes = [i32]
         L.pgg_timing_end.argtypes = [ctypes.POINTER(KernelTime), i32, ctypes.POINTER(i32)]
         L.pgg_status_string.argtypes = [ctypes.c_int]
@@ -125,7 +135,8 @@ def lib():
         for f in ("pgg_moe_dx_workspace_size", "pgg_moe_dx", "pgg_moe_dx_read_device_error",
                   "pgg_moe_dx_debug_tables", "pgg_moe_dx_debug_tiles", "pgg_moe_dx_plan",
                   "pgg_moe_dx_kernel_time", "pgg_moe_fwd_workspace_size", "pgg_moe_fwd",
-                  "pgg_moe_fwd_plan", "pgg_moe_fwd_kernel_time",
+                  "pgg_moe_fwd_plan", "pgg_moe_fwd_kernel_time", "pgg_moe_dw_workspace_size",
+                  "pgg_moe_dw", "pgg_moe_dw_kernel_time",
                   "pgg_timing_begin", "pgg_timing_end"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
@@ -381,6 +392,77 @@ def fwd_kernel_time(x, weight, expanded_row_idx, group_list, topk, row_idx_type=
                                          workspace.numel() * workspace.element_size(),
                                          _stream_handle(stream), int(repeats), ctypes.byref(avg)),
            "fwd_kernel_time")
+    return avg.value
+
+
+# ---------------------------------------------------------------- weight gradient
+
+def _dw_desc_from_tensors(x, grad_y, eri, group_list, topk, row_idx_type) -> FwdDesc:
+    if x.dim() != 2 or grad_y.dim() != 2 or eri.dim() != 1 or group_list.dim() != 1:
+        raise PggError(ERR_INVALID_ARG, "rank")
+    if eri.dtype != torch.int64 or group_list.dtype != torch.int64:
+        raise PggError(ERR_INVALID_ARG, "index dtype")
+    if grad_y.shape[0] != x.shape[0] * int(topk):
+        raise PggError(ERR_INVALID_ARG, "grad_y must be [batch*topk, N]")
+    G = group_list.shape[0]
+    return make_fwd_desc(x.shape, (G, x.shape[1], grad_y.shape[1]), eri.shape[0], G, x.shape[0], topk,
+                         row_idx_type, DTYPE_CODE.get(x.dtype, -1), DTYPE_CODE.get(grad_y.dtype, -1))
+
+
+def dw_workspace_size(x, grad_y, expanded_row_idx, group_list, topk, row_idx_type=0) -> int:
+    d = _dw_desc_from_tensors(x, grad_y, expanded_row_idx, group_list, topk, row_idx_type)
+    n = ctypes.c_size_t()
+    _check(lib().pgg_moe_dw_workspace_size(ctypes.byref(d), ctypes.byref(n)), "dw_workspace_size")
+    return n.value
+
+
+def _dw_buffers(d, x, out, workspace):
+    dev = x.device
+    if workspace is None:
+        n = ctypes.c_size_t()
+        _check(lib().pgg_moe_dw_workspace_size(ctypes.byref(d), ctypes.byref(n)), "dw_workspace_size")
+        workspace = torch.empty(n.value, dtype=torch.uint8, device=dev)
+    shape = (int(d.weight_groups), int(d.weight_rows), int(d.weight_cols))
+    if out is None:
+        out = torch.empty(shape, dtype=torch.float32, device=dev)
+    if out.dtype != torch.float32 or not out.is_contiguous() or tuple(out.shape) != shape:
+        raise PggError(ERR_INVALID_ARG, "out must be a contiguous float32 [G, K, N] tensor")
+    return out, workspace
+
+
+def moe_dw(x: torch.Tensor, grad_y: torch.Tensor, expanded_row_idx: torch.Tensor,
+           group_list: torch.Tensor, topk: int, row_idx_type: int = 0, *,
+           out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+           stream=None) -> torch.Tensor:
+    """Weight gradient: float32 grad_w [G, K, N], grad_w[g] = (x rows of expert
+    g's expanded rows)^T · grad_y[those rows] (asynchronous).  x [batch, K] and
+    grad_y [batch*topk, N] share one of float32 / float16 / bfloat16."""
+    d = _dw_desc_from_tensors(x, grad_y, expanded_row_idx, group_list, topk, row_idx_type)
+    for t in (x, grad_y, expanded_row_idx, group_list):
+        if not t.is_cuda or not t.is_contiguous():
+            raise PggError(ERR_INVALID_ARG, "inputs must be contiguous GPU tensors")
+    out, workspace = _dw_buffers(d, x, out, workspace)
+    st = lib().pgg_moe_dw(ctypes.byref(d), x.data_ptr(), grad_y.data_ptr(),
+                          expanded_row_idx.data_ptr(), group_list.data_ptr(), out.data_ptr(),
+                          workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                          _stream_handle(stream))
+    _check(st, "pgg_moe_dw")
+    return out
+
+
+def dw_kernel_time(x, grad_y, expanded_row_idx, group_list, topk, row_idx_type=0, *,
+                   repeats: int = 10, out=None, workspace=None, stream=None) -> float:
+    """Average ms of one launch of the weight-gradient kernel, back to back
+    after one full call (pgg_moe_dw_kernel_time)."""
+    d = _dw_desc_from_tensors(x, grad_y, expanded_row_idx, group_list, topk, row_idx_type)
+    out, workspace = _dw_buffers(d, x, out, workspace)
+    avg = ctypes.c_double()
+    _check(lib().pgg_moe_dw_kernel_time(ctypes.byref(d), x.data_ptr(), grad_y.data_ptr(),
+                                        expanded_row_idx.data_ptr(), group_list.data_ptr(),
+                                        out.data_ptr(), workspace.data_ptr(),
+                                        workspace.numel() * workspace.element_size(),
+                                        _stream_handle(stream), int(repeats), ctypes.byref(avg)),
+           "dw_kernel_time")
     return avg.value
 
 

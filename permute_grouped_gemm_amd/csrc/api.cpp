@@ -1,5 +1,5 @@
-// C ABI of the fused MoE d_x backward and of the layer's forward (declared
-// in include/pgg.h).
+// C ABI of the fused MoE d_x backward, of the layer's forward and of its
+// weight gradient (declared in include/pgg.h).
 //
 // The execute call validates the descriptor on the host, lays out the
 // workspace, and enqueues on the caller's stream:
@@ -145,9 +145,9 @@ pgg_status enqueue(const Call& c, const void* grad_y, const void* weight,
 
 pgg_status check_fwd(const pgg_moe_fwd_desc* desc, const void* x, const void* weight,
                      const int64_t* expanded_row_idx, const int64_t* group_list, const float* y,
-                     void* workspace, size_t workspace_bytes, Call* c) {
+                     void* workspace, size_t workspace_bytes, Call* c, bool dw = false) {
   Plan& p = c->plan;
-  const pgg_status st = make_fwd_plan(desc, &p);
+  const pgg_status st = dw ? make_dw_plan(desc, &p) : make_fwd_plan(desc, &p);
   if (st != PGG_OK) return st;
   if (!x || !weight || !expanded_row_idx || !group_list || !y || !workspace)
     return PGG_ERR_INVALID_ARG;
@@ -176,6 +176,27 @@ pgg_status enqueue_fwd(const Call& c, const void* x, const void* weight,
   if (e == hipSuccess && p.ksplit > 1) {
     TimedLaunch t("forward_reduce", stream);
     e = launch_forward_reduce(p, c.w, y, stream);
+  }
+  return e == hipSuccess ? PGG_OK : PGG_ERR_HIP;
+}
+
+// The weight gradient: same checks as the forward, with grad_y in the
+// weight's place (its rows hold N elements, as the weight's rows do).
+pgg_status check_dw(const pgg_moe_fwd_desc* desc, const void* x, const void* grad_y,
+                    const int64_t* expanded_row_idx, const int64_t* group_list, const float* dw,
+                    void* workspace, size_t workspace_bytes, Call* c) {
+  return check_fwd(desc, x, grad_y, expanded_row_idx, group_list, dw, workspace, workspace_bytes, c,
+                   true);
+}
+
+pgg_status enqueue_dw(const Call& c, const void* x, const void* grad_y,
+                      const int64_t* expanded_row_idx, const int64_t* group_list, float* dw,
+                      hipStream_t stream) {
+  const Plan& p = c.plan;
+  hipError_t e = enqueue_prep(p, expanded_row_idx, group_list, c.w, stream);
+  if (e == hipSuccess) {
+    TimedLaunch t(dw_kernel_name(p), stream);
+    e = launch_dw(p, x, grad_y, dw, c.aligned, c.w, stream);
   }
   return e == hipSuccess ? PGG_OK : PGG_ERR_HIP;
 }
@@ -320,6 +341,54 @@ pgg_status pgg_moe_fwd_kernel_time(const pgg_moe_fwd_desc* desc, const void* x, 
   hipError_t e = st == PGG_OK ? hipEventRecord(ev[0], stream) : hipErrorUnknown;
   for (int32_t r = 0; r < repeats && e == hipSuccess; ++r)
     e = launch_forward(c.plan, x, weight, y, c.aligned, c.w, stream);
+  if (e == hipSuccess) e = hipEventRecord(ev[1], stream);
+  if (e == hipSuccess) e = hipEventSynchronize(ev[1]);
+  float ms = 0.0f;
+  if (e == hipSuccess) e = hipEventElapsedTime(&ms, ev[0], ev[1]);
+  for (auto& x_ev : ev)
+    if (x_ev) (void)hipEventDestroy(x_ev);
+  if (st != PGG_OK) return st;
+  if (e != hipSuccess) return PGG_ERR_HIP;
+  *avg_ms = double(ms) / double(repeats);
+  return PGG_OK;
+}
+
+pgg_status pgg_moe_dw_workspace_size(const pgg_moe_fwd_desc* desc, size_t* bytes) {
+  if (!bytes) return PGG_ERR_INVALID_ARG;
+  Plan p;
+  const pgg_status st = make_dw_plan(desc, &p);
+  if (st != PGG_OK) return st;
+  *bytes = p.total;
+  return PGG_OK;
+}
+
+pgg_status pgg_moe_dw(const pgg_moe_fwd_desc* desc, const void* x, const void* grad_y,
+                      const int64_t* expanded_row_idx, const int64_t* group_list, float* grad_w,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  Call c;
+  const pgg_status st = check_dw(desc, x, grad_y, expanded_row_idx, group_list, grad_w, workspace,
+                                 workspace_bytes, &c);
+  if (st != PGG_OK) return st;
+  return enqueue_dw(c, x, grad_y, expanded_row_idx, group_list, grad_w, stream);
+}
+
+pgg_status pgg_moe_dw_kernel_time(const pgg_moe_fwd_desc* desc, const void* x, const void* grad_y,
+                                  const int64_t* expanded_row_idx, const int64_t* group_list,
+                                  float* grad_w, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream, int32_t repeats, double* avg_ms) {
+  if (repeats <= 0 || !avg_ms) return PGG_ERR_INVALID_ARG;
+  Call c;
+  pgg_status st = check_dw(desc, x, grad_y, expanded_row_idx, group_list, grad_w, workspace,
+                           workspace_bytes, &c);
+  if (st != PGG_OK) return st;
+  st = enqueue_dw(c, x, grad_y, expanded_row_idx, group_list, grad_w, stream);
+  if (st != PGG_OK) return st;
+  hipEvent_t ev[2] = {nullptr, nullptr};
+  for (auto& e : ev)
+    if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) st = PGG_ERR_HIP;
+  hipError_t e = st == PGG_OK ? hipEventRecord(ev[0], stream) : hipErrorUnknown;
+  for (int32_t r = 0; r < repeats && e == hipSuccess; ++r)
+    e = launch_dw(c.plan, x, grad_y, grad_w, c.aligned, c.w, stream);
   if (e == hipSuccess) e = hipEventRecord(ev[1], stream);
   if (e == hipSuccess) e = hipEventSynchronize(ev[1]);
   float ms = 0.0f;

@@ -70,6 +70,8 @@ struct Plan {
 pgg_status make_plan(const pgg_moe_dx_desc* desc, Plan* plan);
 // The forward's plan: one chunk holding every m-tile, no ring.
 pgg_status make_fwd_plan(const pgg_moe_fwd_desc* desc, Plan* plan);
+// The weight gradient's plan: the forward's validation and tables, no partials.
+pgg_status make_dw_plan(const pgg_moe_fwd_desc* desc, Plan* plan);
 
 // Views of the workspace regions.
 struct WsView {
@@ -134,6 +136,11 @@ hipError_t launch_forward(const Plan& p, const void* x, const void* weight, floa
                           const WsView& w, hipStream_t s);
 const char* forward_kernel_name(const Plan& p);
 // 256x256 direct-to-LDS forward tile (16-bit types, 16-byte aligned rows).
+// Weight gradient dW[g] = (rows of x gathered for expert g)^T · d_y[rows of g].
+hipError_t launch_dw(const Plan& p, const void* x, const void* grad_y, float* dw, bool aligned,
+                     const WsView& w, hipStream_t s);
+const char* dw_kernel_name(const Plan& p);
+
 // Sum of the forward's reduction splits, in split order, into y.
 hipError_t launch_forward_reduce(const Plan& p, const WsView& w, float* y, hipStream_t s);
 hipError_t launch_forward_large(const Plan& p, const void* x, const void* weight, float* y,

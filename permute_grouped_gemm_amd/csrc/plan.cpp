@@ -191,4 +191,17 @@ pgg_status make_fwd_plan(const pgg_moe_fwd_desc* d, Plan* p) {
   return PGG_OK;
 }
 
+pgg_status make_dw_plan(const pgg_moe_fwd_desc* d, Plan* p) {
+  Plan q;
+  const pgg_status st = make_fwd_plan(d, &q);
+  if (st != PGG_OK) return st;
+  q.ksplit = 1;
+  q.kspan = static_cast<int32_t>(q.N);
+  q.ring_rows = 0;
+  q.ring_bytes = 0;
+  q.total = q.table_bytes;
+  *p = q;
+  return PGG_OK;
+}
+
 }  // namespace pgg
