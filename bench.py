@@ -20,8 +20,9 @@ launch's dispatch latency to every measurement.  The CPU baseline is the oracle 
 workload, timed on this host.
 
 Each workload also reports the layer's forward (Permute + GroupedMatmul,
-pgg_moe_fwd) on its routing and weights under "forward" (--no-forward skips
-it); the headline value stays the fused backward's.
+pgg_moe_fwd) under "forward" and its weight gradient (pgg_moe_dw) under
+"dweight", on the workload's routing, weights and d_y (--no-forward skips
+both); the headline value stays the fused backward's.
 """
 from __future__ import annotations
 
@@ -154,6 +155,76 @@ def measure_forward(case, w, eri, gl, steps, log):
             "algorithmic_bytes": bytes_, "flops": flops, "plan": plan,
             "what": "y[i,n] = sum_k x[p(i)//topK, k] W[g(i),k,n] on the workload's routing and "
                     "weights, x ~ N(0,1) seeded; time covers the index preparation and the kernel"}
+
+
+def algorithmic_dw(case):
+    """Algorithmic flops and bytes of one weight-gradient call: x (each token row
+    once) + d_y + grad_w written once (fp32, all G experts); flops = 2*M*K*N."""
+    s = {"f32": 4, "f16": 2, "bf16": 2}[case.dtype]
+    flops = 2.0 * case.M * case.N * case.K
+    kernel_bytes = case.batch * case.K * s + case.M * case.N * s + 4 * case.G * case.K * case.N
+    return flops, kernel_bytes + 8 * case.M + 8 * case.G, kernel_bytes
+
+
+def measure_dw(case, gy, eri, gl, steps, log):
+    """The weight gradient (expanded_x^T · d_y per expert) on the workload's
+    routing and upstream gradient, with the forward's seeded activations x."""
+    import numpy as np
+    import torch
+
+    import permute_grouped_gemm_amd as pgg
+    import synth
+
+    dev = gy.device
+    x = synth.forward_input(case)
+    if case.dtype == "bf16":
+        xt = torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+    else:
+        xt = torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+    ws = torch.empty(pgg.dw_workspace_size(xt, gy, eri, gl, case.topk, case.row_idx_type),
+                     dtype=torch.uint8, device=dev)
+    out = torch.empty((case.G, case.K, case.N), dtype=torch.float32, device=dev)
+
+    def step():
+        pgg.moe_dw(xt, gy, eri, gl, case.topk, case.row_idx_type, out=out, workspace=ws)
+
+    t_settle = time.time()
+    while time.time() - t_settle < SETTLE_S:
+        for _ in range(4):
+            step()
+        torch.cuda.synchronize()
+    code, detail = pgg.read_device_error(ws)
+    if code != 0:
+        raise RuntimeError(f"weight-gradient device error {code} ({detail})")
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        step()
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    k_ms = pgg.dw_kernel_time(xt, gy, eri, gl, case.topk, case.row_idx_type, repeats=steps, out=out,
+                              workspace=ws)
+    flops, bytes_, kernel_bytes = algorithmic_dw(case)
+    if case.M <= 64 * case.G:
+        achieved = kernel_bytes / (k_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS}
+    else:
+        peak = PEAK_TFLOPS[case.dtype]
+        achieved = flops / (k_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                "frac": achieved / peak}
+    roof.update({"kernel": "dweight", "avg_launch_us": k_ms * 1e3, "launches_per_step": 1})
+    log(f"[bench] {case.name} weight gradient: {ms * 1e3:.1f} us/call, dweight {k_ms * 1e3:.1f} us "
+        f"(back to back), {flops / (ms * 1e-3) / 1e12:.1f} TFLOP/s, {bytes_ / (ms * 1e-3) / 1e9:.0f} GB/s")
+    return {"ms_per_call": ms, "tflops": flops / (ms * 1e-3) / 1e12,
+            "gbs": bytes_ / (ms * 1e-3) / 1e9, "roofline": roof,
+            "algorithmic_bytes": bytes_, "flops": flops,
+            "what": "grad_w[g] = (x rows of expert g)^T d_y[rows of g], fp32 [G,K,N], on the "
+                    "workload's routing and d_y, x ~ N(0,1) seeded; time covers the index "
+                    "preparation and the kernel"}
 
 
 def measure(name, steps, warmup, cpu_baseline, log, forward=True):
@@ -299,6 +370,7 @@ def measure(name, steps, warmup, cpu_baseline, log, forward=True):
     }
     if forward:
         res["forward"] = measure_forward(case, w, eri, gl, steps, log)
+        res["dweight"] = measure_dw(case, gy, eri, gl, steps, log)
     if cpu_baseline:
         res["cpu_baseline"] = oracle_baseline(case, unit, log)
     return res
@@ -439,7 +511,7 @@ def main():
     ap.add_argument("--no-large", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-forward", action="store_true",
-                    help="skip the forward (Permute + GroupedMatmul) measurement")
+                    help="skip the forward and weight-gradient measurements")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--vendor-gemm", action="store_true",
@@ -482,8 +554,9 @@ def main():
                                               "kernels_event_bracketed_ms_per_step",
                                               "workspace_bytes", "ring_bytes",
                                               "d_expanded_x_fp32_bytes", "plan")}
-    if "forward" in primary:
-        line["forward"] = primary["forward"]
+    for k in ("forward", "dweight"):
+        if k in primary:
+            line[k] = primary[k]
     if not args.no_large and args.workload != "large_f16":
         large = measure("large_f16", max(5, args.steps // 2), args.warmup,
                         not args.no_cpu_baseline, log, forward=not args.no_forward)
@@ -495,8 +568,9 @@ def main():
                                                "d_expanded_x_fp32_bytes", "config", "dtype")}
         if "cpu_baseline" in large:
             line["large"]["cpu_baseline"] = large["cpu_baseline"]
-        if "forward" in large:
-            line["large"]["forward"] = large["forward"]
+        for k in ("forward", "dweight"):
+            if k in large:
+                line["large"][k] = large[k]
     print(json.dumps(line), flush=True)
     return 0
 

@@ -92,6 +92,8 @@ void dw_kernel(DwArgs a) {
   const int lr = lane & 31;
   const int lh = lane >> 5;
 
+  // topK and positions are below M < 2^31: 32-bit unsigned division
+  const uint32_t topk32 = static_cast<uint32_t>(a.topk);
   u32x4_t ra[PER_T], rb[PER_T];
   auto load_stage = [&](int kt) {
     const int64_t i0 = r_begin + static_cast<int64_t>(kt) * BK;
@@ -101,7 +103,7 @@ void dw_kernel(DwArgs a) {
       const int r = q / kRowChunks, c = q % kRowChunks;
       const int64_t i = i0 + r;
       const bool ok = i < r_end;
-      const int64_t tok = ok ? a.ori[i] / a.topk : 0;
+      const int64_t tok = ok ? static_cast<uint32_t>(a.ori[i]) / topk32 : 0;
       ra[s] = load_chunk<T, ALIGNED>(X + tok * K, ok, k0 + c * EPC, K);
       rb[s] = load_chunk<T, ALIGNED>(DY + (ok ? i : 0) * N, ok, n0 + c * EPC, N);
     }

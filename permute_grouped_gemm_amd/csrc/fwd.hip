@@ -126,11 +126,13 @@ void fwd_kernel(FwdArgs a) {
 
   // Gathered A rows of this thread's staging slots: chunk id q -> (row q / 8,
   // chunk q % 8); row r of the tile is token ori[row0 + r] / topK of x.
+  // topK and positions are below M < 2^31: 32-bit unsigned division
+  const uint32_t topk32 = static_cast<uint32_t>(a.topk);
   const E* arow[A_PER_T];
 #pragma unroll
   for (int s = 0; s < A_PER_T; ++s) {
     const int r = (tid + s * NT) / kChunks;
-    const int64_t tok = r < rows ? a.ori[tile.row0 + r] / a.topk : 0;
+    const int64_t tok = r < rows ? static_cast<uint32_t>(a.ori[tile.row0 + r]) / topk32 : 0;
     arow[s] = X + tok * RX;
   }
 

@@ -110,13 +110,15 @@ void fwd_large_kernel(FwdLargeArgs a) {
   // which holds chunk dma_c (the same for every j).
   const int r0 = wave * kRowsPerLoad + (lane >> 3);
   const int dma_c = slot_of(r0, lane & 7);
+  // topK and positions are below M < 2^31: 32-bit unsigned division
+  const uint32_t topk32 = static_cast<uint32_t>(a.topk);
   const E* pa[kLoadsA];
   uint32_t va = 0;
 #pragma unroll
   for (int j = 0; j < kLoadsA; ++j) {
     const int r = r0 + kLoadRows * j;
     const bool ok = r < rows;
-    const int64_t tok = ok ? a.ori[tile.row0 + r] / a.topk : 0;
+    const int64_t tok = ok ? static_cast<uint32_t>(a.ori[tile.row0 + r]) / topk32 : 0;
     pa[j] = static_cast<const E*>(a.X) + tok * R + dma_c * 8;
     va |= (ok ? 1u : 0u) << j;
   }
