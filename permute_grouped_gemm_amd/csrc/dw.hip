@@ -21,7 +21,8 @@
 // fp32.  Stages are double-buffered in LDS with a register prefetch of the
 // next stage.  Row tails (the expert's last stage), k and n tails are
 // zero-filled on load and masked on store; ALIGNED=false handles rows that
-// are not 16-byte aligned with element loads.
+// are not 16-byte aligned with element loads.  Aligned 16-bit rows with many
+// rows per expert take the direct-to-LDS tile of dw_large.hip instead.
 #include "pgg_device.h"
 
 namespace pgg {
@@ -238,6 +239,9 @@ hipError_t launch_dw(const Plan& p, const void* x, const void* grad_y, float* dw
   a.N = p.K;            // and the weight's last dimension (N) in K
   a.topk = p.topk;
   if (p.dtype == PGG_F32) return launch_typed<TF32, 128, 128, 2, 2>(p, a, aligned, s);
+  // many rows per expert: the direct-to-LDS tile; with few, every tile is
+  // one or two stages and the register-staged tile is as fast
+  if (aligned && p.regime == kLarge) return launch_dw_large(p, x, grad_y, dw, w, s);
   if (p.dtype == PGG_BF16) return launch_typed<TBf16, 256, 256, 2, 2>(p, a, aligned, s);
   return launch_typed<TF16, 256, 256, 2, 2>(p, a, aligned, s);
 }

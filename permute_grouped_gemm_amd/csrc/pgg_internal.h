@@ -140,6 +140,9 @@ const char* forward_kernel_name(const Plan& p);
 hipError_t launch_dw(const Plan& p, const void* x, const void* grad_y, float* dw, bool aligned,
                      const WsView& w, hipStream_t s);
 const char* dw_kernel_name(const Plan& p);
+// Direct-to-LDS weight-gradient tile (16-bit types, 16-byte aligned rows).
+hipError_t launch_dw_large(const Plan& p, const void* x, const void* grad_y, float* dw,
+                           const WsView& w, hipStream_t s);
 
 // Sum of the forward's reduction splits, in split order, into y.
 hipError_t launch_forward_reduce(const Plan& p, const WsView& w, float* y, hipStream_t s);
