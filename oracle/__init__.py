@@ -307,6 +307,41 @@ def case_dw(case, x, **kw):
                   case.row_idx_type, case.dtype, **kw)
 
 
+def moe_routing(expert_ids, G):
+    """MoeInitRouting's index outputs from the router's choices (CPU, plain loops).
+
+    MoeInitRoutingGroupedMatmulGrad design page, §1.1 step 1 (MoeInitRouting,
+    semantically a permute: tokens are grouped by expert) with the original
+    position p = b * topK + j of §数学定义和公式.  Expanded rows are grouped by
+    expert in expert order, and inside an expert they keep ascending p (the
+    page fixes no order there; this stable order is the reading taken).
+    Returns (group_list int64 [G] counts, eri_type0 int64 [M]: original
+    position of each expanded row, eri_type1 int64 [M]: expanded row of each
+    position).  Raises OracleError(ERR_INDEX_RANGE) for an id outside [0, G).
+    """
+    ids = np.asarray(expert_ids, dtype=np.int64).reshape(-1)
+    M = ids.size
+    counts = [0] * G
+    for p in range(M):
+        e = int(ids[p])
+        if e < 0 or e >= G:
+            raise OracleError(ERR_INDEX_RANGE, f"expert id {e} at position {p}")
+        counts[e] += 1
+    start = [0] * G
+    for g in range(1, G):
+        start[g] = start[g - 1] + counts[g - 1]
+    nxt = list(start)
+    type0 = np.empty(M, dtype=np.int64)
+    type1 = np.empty(M, dtype=np.int64)
+    for p in range(M):                       # ascending p: a stable placement
+        e = int(ids[p])
+        row = nxt[e]
+        nxt[e] += 1
+        type0[row] = p
+        type1[p] = row
+    return np.array(counts, dtype=np.int64), type0, type1
+
+
 def case_fwd(case, x, **kw):
     """moe_fwd on a ``synth.Case`` and its forward input x [batch, K]."""
     return moe_fwd(x, case.weight, case.eri, case.group_list, case.batch, case.topk,
