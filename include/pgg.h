@@ -55,7 +55,9 @@ typedef enum {
   PGG_DEV_GROUP_NEGATIVE = 1,       /* group_list[g] < 0; detail = g */
   PGG_DEV_GROUP_SUM = 2,            /* sum(group_list) != M; detail = the sum (clamped to >= 0) */
   PGG_DEV_INDEX_RANGE = 3,          /* expanded_row_idx[t] outside [0, M); detail = t */
-  PGG_DEV_INDEX_DUP = 4             /* expanded_row_idx is not a permutation; detail = a repeated value */
+  PGG_DEV_INDEX_DUP = 4,            /* expanded_row_idx is not a permutation; detail = a repeated value */
+  PGG_DEV_EXPERT_RANGE = 5          /* pgg_moe_routing: an expert id outside [0, experts);
+                                       detail = the smallest such position */
 } pgg_device_error;
 
 /*
@@ -121,7 +123,7 @@ pgg_status pgg_moe_dx(const pgg_moe_dx_desc* desc, const void* grad_y, const voi
 
 /*
  * Read the device error word of the last pgg_moe_dx (or pgg_moe_fwd,
- * pgg_moe_dw) that used `workspace`.
+ * pgg_moe_dw, pgg_moe_routing) that used `workspace`.
  * Synchronises `stream`.  *code receives a pgg_device_error; *detail its
  * detail value (may be NULL).  When several violations exist, the one with
  * the smallest (code, detail) is reported, so the report is deterministic.
@@ -313,6 +315,42 @@ pgg_status pgg_moe_dw_kernel_time(const pgg_moe_fwd_desc* desc, const void* x, c
                                   const int64_t* expanded_row_idx, const int64_t* group_list,
                                   float* grad_w, void* workspace, size_t workspace_bytes,
                                   hipStream_t stream, int32_t repeats, double* avg_ms);
+
+/*
+ * MoeInitRouting on the device (MoeInitRoutingGroupedMatmulGrad design page,
+ * §1.1 step 1: tokens grouped by expert, semantically a permute; original
+ * position p = b*topK + j as in §数学定义和公式): from the router's choices
+ * it builds the tables the operators above take.
+ *
+ *   expert_ids   [batch, topk] int64, each in [0, experts)       input
+ *   x            [batch, x_cols] x_dtype (only when x_cols > 0)  input
+ *   group_list   [experts] int64: rows per expert                output
+ *   eri_gather   [M] int64: original position of expanded row i (row_idx_type 0)   output, may be NULL
+ *   eri_scatter  [M] int64: expanded row of position p (row_idx_type 1)            output, may be NULL
+ *   expanded_x   [M, x_cols] x_dtype: row i = x[eri_gather[i] / topk]              output, may be NULL
+ *
+ * Expanded rows are grouped by expert in expert order and keep ascending p
+ * inside an expert (the page fixes no order there; this stable order makes
+ * the tables unique), so repeated calls give identical tables.  An id outside
+ * [0, experts) sets the workspace error word (PGG_DEV_EXPERT_RANGE, read with
+ * pgg_moe_dx_read_device_error); the outputs are then unspecified.  Limits:
+ * experts <= 8192 and M < 2^31 (PGG_ERR_UNSUPPORTED beyond).  Pointers:
+ * expert_ids and the int64 outputs 8-byte aligned, x / expanded_x aligned to
+ * their element size; workspace 256-byte aligned.
+ */
+typedef struct {
+  int64_t batch, topk;
+  int64_t experts;
+  int64_t x_cols;         /* 0: no expanded_x */
+  int32_t x_dtype;        /* pgg_dtype of x and expanded_x when x_cols > 0 */
+  int32_t reserved;       /* must be 0 */
+} pgg_moe_routing_desc;
+
+pgg_status pgg_moe_routing_workspace_size(const pgg_moe_routing_desc* desc, size_t* bytes);
+pgg_status pgg_moe_routing(const pgg_moe_routing_desc* desc, const int64_t* expert_ids,
+                           const void* x, int64_t* group_list, int64_t* eri_gather,
+                           int64_t* eri_scatter, void* expanded_x, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream);
 
 const char* pgg_status_string(pgg_status status);
 const char* pgg_device_error_string(int32_t code);

@@ -21,7 +21,12 @@ GroupedMatmul, y[i,n] = sum_k x[p(i) // topK, k] * weight[g(i),k,n], float32
     grad_w = moe_dw(x, grad_y, expanded_row_idx, group_list, topk, row_idx_type)
 
 is the weight gradient (§1.2's separate operator, expanded_x^T · d_y per
-expert), float32 [G, K, N].
+expert), float32 [G, K, N], and
+
+    group_list, eri_gather, eri_scatter, expanded_x = moe_routing(expert_ids, G, x)
+
+is MoeInitRouting on the device (§1.1 step 1): the routing tables (and the
+permuted x) from the router's choices.
 """
 from __future__ import annotations
 
@@ -35,7 +40,7 @@ import torch
 __all__ = [
     "moe_dx", "workspace_size", "plan", "read_device_error", "debug_tables", "debug_tiles",
     "moe_fwd", "fwd_workspace_size", "fwd_plan", "fwd_kernel_time",
-    "moe_dw", "dw_workspace_size", "dw_kernel_time",
+    "moe_dw", "dw_workspace_size", "dw_kernel_time", "moe_routing",
     "KernelTimer", "PggError", "lib", "LIB_PATH", "HEADER_PATH",
 ]
 
@@ -44,7 +49,7 @@ LIB_PATH = os.path.join(PKG, "libpgg.so")
 HEADER_PATH = os.path.join(os.path.dirname(PKG), "include", "pgg.h")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE_TOO_SMALL, ERR_HIP, ERR_MISALIGNED = range(6)
-DEV_OK, DEV_GROUP_NEGATIVE, DEV_GROUP_SUM, DEV_INDEX_RANGE, DEV_INDEX_DUP = range(5)
+DEV_OK, DEV_GROUP_NEGATIVE, DEV_GROUP_SUM, DEV_INDEX_RANGE, DEV_INDEX_DUP, DEV_EXPERT_RANGE = range(6)
 DTYPE_CODE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 
 
@@ -67,6 +72,13 @@ class FwdDesc(ctypes.Structure):
         ("group_list_len", ctypes.c_int64), ("batch", ctypes.c_int64), ("topk", ctypes.c_int64),
         ("row_idx_type", ctypes.c_int32), ("x_dtype", ctypes.c_int32),
         ("weight_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
+    ]
+
+
+class RoutingDesc(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int64), ("topk", ctypes.c_int64), ("experts", ctypes.c_int64),
+        ("x_cols", ctypes.c_int64), ("x_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
     ]
 
 
@@ -126,6 +138,9 @@ def lib():
         L.pgg_moe_dw.argtypes = [PF, vp, vp, vp, vp, vp, vp, sz, vp]
         L.pgg_moe_dw_kernel_time.argtypes = [PF, vp, vp, vp, vp, vp, vp, sz, vp, i32,
                                               ctypes.POINTER(ctypes.c_double)]
+        PR = ctypes.POINTER(RoutingDesc)
+        L.pgg_moe_routing_workspace_size.argtypes = [PR, ctypes.POINTER(sz)]
+        L.pgg_moe_routing.argtypes = [PR, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.pgg_timing_begin.argtypes = [i32]
         L.pgg_timing_end.argtypes = [ctypes.POINTER(KernelTime), i32, ctypes.POINTER(i32)]
         L.pgg_status_string.argtypes = [ctypes.c_int]
@@ -136,7 +151,8 @@ def lib():
                   "pgg_moe_dx_debug_tables", "pgg_moe_dx_debug_tiles", "pgg_moe_dx_plan",
                   "pgg_moe_dx_kernel_time", "pgg_moe_fwd_workspace_size", "pgg_moe_fwd",
                   "pgg_moe_fwd_plan", "pgg_moe_fwd_kernel_time", "pgg_moe_dw_workspace_size",
-                  "pgg_moe_dw", "pgg_moe_dw_kernel_time",
+                  "pgg_moe_dw", "pgg_moe_dw_kernel_time", "pgg_moe_routing_workspace_size",
+                  "pgg_moe_routing",
                   "pgg_timing_begin", "pgg_timing_end"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
@@ -464,6 +480,56 @@ def dw_kernel_time(x, grad_y, expanded_row_idx, group_list, topk, row_idx_type=0
                                         _stream_handle(stream), int(repeats), ctypes.byref(avg)),
            "dw_kernel_time")
     return avg.value
+
+
+# ---------------------------------------------------------------- routing
+
+def make_routing_desc(batch, topk, experts, x_cols=0, x_dtype=0) -> RoutingDesc:
+    d = RoutingDesc()
+    d.batch, d.topk, d.experts, d.x_cols = int(batch), int(topk), int(experts), int(x_cols)
+    d.x_dtype = int(x_dtype)
+    d.reserved = 0
+    return d
+
+
+def routing_workspace_size_desc(d: RoutingDesc) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().pgg_moe_routing_workspace_size(ctypes.byref(d), ctypes.byref(n)),
+           "routing_workspace_size")
+    return n.value
+
+
+def moe_routing(expert_ids: torch.Tensor, experts: int, x: Optional[torch.Tensor] = None, *,
+                gather: bool = True, scatter: bool = True, workspace=None, stream=None):
+    """MoeInitRouting on the device: (group_list [G], eri_gather [M] or None,
+    eri_scatter [M] or None, expanded_x [M, K] or None) from expert_ids
+    [batch, topk] int64 (asynchronous).  With x [batch, K], expanded_x is the
+    permuted copy of x in expanded-row order."""
+    if expert_ids.dim() != 2 or expert_ids.dtype != torch.int64:
+        raise PggError(ERR_INVALID_ARG, "expert_ids must be an int64 [batch, topk] tensor")
+    if not expert_ids.is_cuda or not expert_ids.is_contiguous():
+        raise PggError(ERR_INVALID_ARG, "expert_ids must be a contiguous GPU tensor")
+    batch, topk = expert_ids.shape
+    K, xd = 0, 0
+    if x is not None:
+        if x.dim() != 2 or x.shape[0] != batch or not x.is_cuda or not x.is_contiguous():
+            raise PggError(ERR_INVALID_ARG, "x must be a contiguous GPU [batch, K] tensor")
+        K, xd = x.shape[1], DTYPE_CODE.get(x.dtype, -1)
+    d = make_routing_desc(batch, topk, experts, K, xd)
+    dev = expert_ids.device
+    if workspace is None:
+        workspace = torch.empty(routing_workspace_size_desc(d), dtype=torch.uint8, device=dev)
+    M = batch * topk
+    gl = torch.empty(int(experts), dtype=torch.int64, device=dev)
+    eg = torch.empty(M, dtype=torch.int64, device=dev) if gather else None
+    es = torch.empty(M, dtype=torch.int64, device=dev) if scatter else None
+    ex = torch.empty((M, K), dtype=x.dtype, device=dev) if x is not None else None
+    ptr = lambda t: None if t is None else t.data_ptr()
+    st = lib().pgg_moe_routing(ctypes.byref(d), expert_ids.data_ptr(), ptr(x), gl.data_ptr(), ptr(eg),
+                               ptr(es), ptr(ex), workspace.data_ptr(),
+                               workspace.numel() * workspace.element_size(), _stream_handle(stream))
+    _check(st, "pgg_moe_routing")
+    return gl, eg, es, ex
 
 
 class KernelTimer:

@@ -1,5 +1,5 @@
-// C ABI of the fused MoE d_x backward, of the layer's forward and of its
-// weight gradient (declared in include/pgg.h).
+// C ABI of the fused MoE d_x backward, of the layer's forward, of its weight
+// gradient and of on-device routing (declared in include/pgg.h).
 //
 // The execute call validates the descriptor on the host, lays out the
 // workspace, and enqueues on the caller's stream:
@@ -401,6 +401,42 @@ pgg_status pgg_moe_dw_kernel_time(const pgg_moe_fwd_desc* desc, const void* x, c
   return PGG_OK;
 }
 
+pgg_status pgg_moe_routing_workspace_size(const pgg_moe_routing_desc* desc, size_t* bytes) {
+  if (!bytes) return PGG_ERR_INVALID_ARG;
+  RoutePlan p;
+  const pgg_status st = make_routing_plan(desc, &p);
+  if (st != PGG_OK) return st;
+  *bytes = p.total;
+  return PGG_OK;
+}
+
+pgg_status pgg_moe_routing(const pgg_moe_routing_desc* desc, const int64_t* expert_ids,
+                           const void* x, int64_t* group_list, int64_t* eri_gather,
+                           int64_t* eri_scatter, void* expanded_x, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  RoutePlan p;
+  const pgg_status st = make_routing_plan(desc, &p);
+  if (st != PGG_OK) return st;
+  if (!expert_ids || !group_list || !workspace) return PGG_ERR_INVALID_ARG;
+  if (expanded_x && (p.K == 0 || !x)) return PGG_ERR_INVALID_ARG;
+  if (workspace_bytes < p.total) return PGG_ERR_WORKSPACE_TOO_SMALL;
+  if (!is_aligned(workspace, kWorkspaceAlign) || !is_aligned(expert_ids, 8) ||
+      !is_aligned(group_list, 8) || (eri_gather && !is_aligned(eri_gather, 8)) ||
+      (eri_scatter && !is_aligned(eri_scatter, 8)))
+    return PGG_ERR_MISALIGNED;
+  const size_t es = elem_size(p.dtype);
+  if (expanded_x && (!is_aligned(x, es) || !is_aligned(expanded_x, es))) return PGG_ERR_MISALIGNED;
+  const bool vec = expanded_x && is_aligned(x, 16) && is_aligned(expanded_x, 16) &&
+                   (size_t(p.K) * es) % 16 == 0;
+  hipError_t e;
+  {
+    TimedLaunch t("routing", stream);
+    e = launch_routing(p, expert_ids, x, group_list, eri_gather, eri_scatter, expanded_x, workspace,
+                       vec, stream);
+  }
+  return e == hipSuccess ? PGG_OK : PGG_ERR_HIP;
+}
+
 pgg_status pgg_moe_dx_read_device_error(const void* workspace, hipStream_t stream, int32_t* code,
                                         int64_t* detail) {
   if (!workspace || !code) return PGG_ERR_INVALID_ARG;
@@ -536,6 +572,7 @@ const char* pgg_device_error_string(int32_t code) {
     case PGG_DEV_GROUP_SUM: return "sum(group_list) != M";
     case PGG_DEV_INDEX_RANGE: return "expanded_row_idx value outside [0, M)";
     case PGG_DEV_INDEX_DUP: return "expanded_row_idx is not a permutation";
+    case PGG_DEV_EXPERT_RANGE: return "expert id outside [0, experts)";
   }
   return "unknown device error";
 }

@@ -130,6 +130,17 @@ hipError_t launch_consume(const Plan& p, int chunk, const WsView& w, float* grad
 
 const char* produce_kernel_name(const Plan& p);
 
+// MoeInitRouting on the device: workspace layout and launches.
+struct RoutePlan {
+  int64_t M, G, topk, K;
+  int32_t dtype, nblocks;
+  size_t off_header, off_table, off_bad, off_offsets, off_ori, total;
+};
+pgg_status make_routing_plan(const pgg_moe_routing_desc* desc, RoutePlan* plan);
+hipError_t launch_routing(const RoutePlan& p, const int64_t* ids, const void* x, int64_t* group_list,
+                          int64_t* eri_gather, int64_t* eri_scatter, void* expanded_x, void* ws,
+                          bool vec, hipStream_t s);
+
 // Forward grouped matmul with the permute gathered into the A operand:
 // y[i, :] = x[ori[i] / topK, :] · W[g(i)] for every m-tile of the plan.
 hipError_t launch_forward(const Plan& p, const void* x, const void* weight, float* y, bool aligned,

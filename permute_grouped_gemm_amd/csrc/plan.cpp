@@ -191,6 +191,35 @@ pgg_status make_fwd_plan(const pgg_moe_fwd_desc* d, Plan* p) {
   return PGG_OK;
 }
 
+pgg_status make_routing_plan(const pgg_moe_routing_desc* d, RoutePlan* p) {
+  if (!d || !p) return PGG_ERR_INVALID_ARG;
+  if (d->reserved != 0 || d->batch <= 0 || d->topk <= 0 || d->experts <= 0 || d->x_cols < 0)
+    return PGG_ERR_INVALID_ARG;
+  if (d->x_cols > 0 && (d->x_dtype < PGG_F32 || d->x_dtype > PGG_BF16)) return PGG_ERR_INVALID_ARG;
+  if (d->topk > INT64_MAX / d->batch) return PGG_ERR_INVALID_ARG;
+  const int64_t M = d->batch * d->topk;
+  constexpr int64_t kBlockPos = 1024;
+  if (M >= (int64_t(1) << 31) - 1 || d->experts > 8192) return PGG_ERR_UNSUPPORTED;
+  const int64_t nblocks = (M + kBlockPos - 1) / kBlockPos;
+  if (nblocks * d->experts >= (int64_t(1) << 28)) return PGG_ERR_UNSUPPORTED;
+  RoutePlan q{};
+  q.M = M;
+  q.G = d->experts;
+  q.topk = d->topk;
+  q.K = d->x_cols;
+  q.dtype = d->x_dtype;
+  q.nblocks = static_cast<int32_t>(nblocks);
+  size_t off = 0;
+  q.off_header = off;  off = align_up(off + sizeof(WsHeader), kRegionAlign);
+  q.off_table = off;   off = align_up(off + sizeof(int32_t) * size_t(nblocks * q.G), kRegionAlign);
+  q.off_bad = off;     off = align_up(off + sizeof(int64_t) * size_t(nblocks), kRegionAlign);
+  q.off_offsets = off; off = align_up(off + sizeof(int64_t) * size_t(q.G + 1), kRegionAlign);
+  q.off_ori = off;     off = align_up(off + sizeof(int32_t) * size_t(M), kRegionAlign);
+  q.total = off;
+  *p = q;
+  return PGG_OK;
+}
+
 pgg_status make_dw_plan(const pgg_moe_fwd_desc* d, Plan* p) {
   Plan q;
   const pgg_status st = make_fwd_plan(d, &q);

@@ -1,0 +1,195 @@
+// MoeInitRouting on the device (MoeInitRoutingGroupedMatmulGrad design page,
+// §1.1 step 1: tokens are grouped by expert, semantically a permute; positions
+// p = b * topK + j as in §数学定义和公式).  From the router's choices
+// expert_ids [batch, topK] it builds:
+//   group_list[g]  rows of expert g (counts);
+//   eri_gather[i]  original position of expanded row i (row_idx_type 0);
+//   eri_scatter[p] expanded row of position p (row_idx_type 1);
+//   expanded_x[i]  = x[eri_gather[i] / topK] (optional).
+// Expanded rows are grouped by expert in expert order and keep ascending p
+// inside an expert, so the tables are unique and reproducible.
+//
+// Four launches: per-block histograms (LDS integer counters; the counts do
+// not depend on the order the adds land in), one workgroup turning them into
+// per-block bases and expert offsets, a placement pass in which one wave per
+// block walks its positions in order (a lane's rank among the earlier lanes
+// of the same expert comes from comparing lane by lane, and the last lane of
+// each expert advances that expert's running count), and the optional row
+// gather.  An id outside [0, G) sets the workspace error word (the smallest
+// offending position wins) and leaves the outputs unspecified.
+#include "pgg_device.h"
+
+namespace pgg {
+
+namespace {
+
+constexpr int kBlockPos = 1024;     // positions per block
+constexpr int kCountThreads = 256;
+constexpr int kScanThreads = 1024;
+constexpr int64_t kNoBad = INT64_MAX;
+constexpr int kMaxExperts = 8192;   // the planner's limit; per-expert LDS arrays are static
+
+__global__ __launch_bounds__(kCountThreads) void route_count_kernel(const int64_t* ids, int64_t M,
+                                                                    int32_t G, int32_t* table,
+                                                                    int64_t* bad) {
+  __shared__ int32_t hist[kMaxExperts];
+  __shared__ unsigned long long s_bad;
+  for (int g = threadIdx.x; g < G; g += blockDim.x) hist[g] = 0;
+  if (threadIdx.x == 0) s_bad = static_cast<unsigned long long>(kNoBad);
+  __syncthreads();
+  const int64_t p0 = static_cast<int64_t>(blockIdx.x) * kBlockPos;
+  for (int t = threadIdx.x; t < kBlockPos; t += blockDim.x) {
+    const int64_t p = p0 + t;
+    if (p >= M) break;
+    const int64_t e = ids[p];
+    if (e >= 0 && e < G)
+      atomicAdd(&hist[e], 1);
+    else
+      atomicMin(&s_bad, static_cast<unsigned long long>(p));
+  }
+  __syncthreads();
+  for (int g = threadIdx.x; g < G; g += blockDim.x)
+    table[static_cast<int64_t>(blockIdx.x) * G + g] = hist[g];
+  if (threadIdx.x == 0) bad[blockIdx.x] = static_cast<int64_t>(s_bad);
+}
+
+// One workgroup: header reset, per-block exclusive bases (in place), counts,
+// expert offsets, and the range error.
+__global__ __launch_bounds__(kScanThreads) void route_scan_kernel(WsHeader* hdr, int32_t* table,
+                                                                  const int64_t* bad, int32_t nblocks,
+                                                                  int32_t G, int64_t* offsets,
+                                                                  int64_t* group_list) {
+  __shared__ long long s_part[kScanThreads];
+  __shared__ long long s_bad[kScanThreads];
+  const int tid = threadIdx.x;
+  if (tid == 0) {
+    hdr->err = kNoError;
+    hdr->n_tiles = 0;
+  }
+  // per expert: exclusive prefix over blocks; thread t owns a contiguous run of experts
+  const int per = (G + kScanThreads - 1) / kScanThreads;
+  const int g0 = min(G, tid * per), g1 = min(G, g0 + per);
+  long long mine = 0;
+  for (int g = g0; g < g1; ++g) {
+    int64_t run = 0;
+    for (int32_t b = 0; b < nblocks; ++b) {
+      int32_t* c = &table[static_cast<int64_t>(b) * G + g];
+      const int32_t v = *c;
+      *c = static_cast<int32_t>(run);
+      run += v;
+    }
+    group_list[g] = run;
+    mine += run;
+  }
+  long long mbad = kNoBad;
+  for (int32_t b = tid; b < nblocks; b += kScanThreads) mbad = bad[b] < mbad ? bad[b] : mbad;
+  s_part[tid] = mine;
+  s_bad[tid] = mbad;
+  __syncthreads();
+  // exclusive scan of the threads' expert totals (threads own ascending experts)
+  for (int d = 1; d < kScanThreads; d <<= 1) {
+    const long long v = tid >= d ? s_part[tid - d] : 0;
+    const long long w = tid + d < kScanThreads ? s_bad[tid + d] : kNoBad;
+    __syncthreads();
+    s_part[tid] += v;
+    s_bad[tid] = w < s_bad[tid] ? w : s_bad[tid];
+    __syncthreads();
+  }
+  int64_t base = s_part[tid] - mine;
+  for (int g = g0; g < g1; ++g) {
+    offsets[g] = base;
+    base += group_list[g];
+  }
+  if (tid == kScanThreads - 1) offsets[G] = s_part[tid];
+  // the word was reset above by this thread: a plain store of (code << 48) | detail
+  if (tid == 0 && s_bad[0] != kNoBad)
+    hdr->err = (static_cast<unsigned long long>(PGG_DEV_EXPERT_RANGE) << kErrShift) |
+               (static_cast<unsigned long long>(s_bad[0]) & kDetailMask);
+}
+
+// One wave per block: positions in order, 64 at a time.
+__global__ __launch_bounds__(64) void route_place_kernel(const WsHeader* hdr, const int64_t* ids,
+                                                         int64_t M, int32_t G, const int32_t* table,
+                                                         const int64_t* offsets, int32_t* ori,
+                                                         int64_t* eri_gather, int64_t* eri_scatter) {
+  __shared__ int32_t run[kMaxExperts];
+  if (hdr->err != kNoError) return;
+  const int lane = threadIdx.x;
+  for (int g = lane; g < G; g += 64)
+    run[g] = static_cast<int32_t>(offsets[g]) + table[static_cast<int64_t>(blockIdx.x) * G + g];
+  __syncthreads();
+  const int64_t p0 = static_cast<int64_t>(blockIdx.x) * kBlockPos;
+  for (int c = 0; c < kBlockPos / 64; ++c) {
+    const int64_t p = p0 + c * 64 + lane;
+    const int32_t e = p < M ? static_cast<int32_t>(ids[p]) : -1;
+    int rank = 0, cnt = 0;
+    for (int j = 0; j < 64; ++j) {
+      const int32_t ej = __builtin_amdgcn_readlane(e, j);
+      if (ej == e) {
+        cnt += 1;
+        if (j < lane) rank += 1;
+      }
+    }
+    int32_t row = 0;
+    if (e >= 0) {
+      row = run[e] + rank;
+      ori[row] = static_cast<int32_t>(p);
+      if (eri_gather) eri_gather[row] = p;
+      if (eri_scatter) eri_scatter[p] = row;
+    }
+    __syncthreads();                       // every lane has read run[] for this chunk
+    if (e >= 0 && rank == cnt - 1) run[e] += cnt;
+    __syncthreads();
+  }
+}
+
+// expanded_x[i] = x[ori[i] / topK]: one workgroup per row, 16-byte pieces when
+// rows are 16-byte aligned.
+__global__ __launch_bounds__(256) void route_gather_kernel(const WsHeader* hdr, const int32_t* ori,
+                                                           int64_t topk, const char* x, char* ex,
+                                                           int64_t row_bytes, int32_t vec) {
+  if (hdr->err != kNoError) return;
+  const int64_t i = blockIdx.x;
+  const int64_t tok = static_cast<uint32_t>(ori[i]) / static_cast<uint32_t>(topk);
+  const char* src = x + tok * row_bytes;
+  char* dst = ex + i * row_bytes;
+  if (vec) {
+    for (int64_t b = threadIdx.x * 16; b < row_bytes; b += 256 * 16)
+      *reinterpret_cast<u32x4_t*>(dst + b) = *reinterpret_cast<const u32x4_t*>(src + b);
+  } else {
+    for (int64_t b = threadIdx.x; b < row_bytes; b += 256) dst[b] = src[b];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_routing(const RoutePlan& p, const int64_t* ids, const void* x, int64_t* group_list,
+                          int64_t* eri_gather, int64_t* eri_scatter, void* expanded_x, void* ws,
+                          bool vec, hipStream_t s) {
+  char* b = static_cast<char*>(ws);
+  WsHeader* hdr = reinterpret_cast<WsHeader*>(b + p.off_header);
+  int32_t* table = reinterpret_cast<int32_t*>(b + p.off_table);
+  int64_t* bad = reinterpret_cast<int64_t*>(b + p.off_bad);
+  int64_t* offsets = reinterpret_cast<int64_t*>(b + p.off_offsets);
+  int32_t* ori = reinterpret_cast<int32_t*>(b + p.off_ori);
+  hipLaunchKernelGGL(route_count_kernel, dim3(p.nblocks), dim3(kCountThreads), 0, s, ids,
+                     p.M, static_cast<int32_t>(p.G), table, bad);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, hdr, table, bad,
+                     p.nblocks, static_cast<int32_t>(p.G), offsets, group_list);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(route_place_kernel, dim3(p.nblocks), dim3(64), 0, s, hdr, ids, p.M,
+                     static_cast<int32_t>(p.G), table, offsets, ori, eri_gather, eri_scatter);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (expanded_x && p.K > 0) {
+    const int64_t row_bytes = p.K * (p.dtype == PGG_F32 ? 4 : 2);
+    hipLaunchKernelGGL(route_gather_kernel, dim3(static_cast<unsigned>(p.M)), dim3(256), 0, s, hdr,
+                       ori, p.topk, static_cast<const char*>(x), static_cast<char*>(expanded_x),
+                       row_bytes, vec ? 1 : 0);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+}  // namespace pgg

@@ -182,3 +182,29 @@ def test_forward_execute_rejects_before_any_launch():
     assert L.pgg_moe_fwd(ctypes.byref(d), fake, fake, fake, fake, fake + 2, fake, need, None) == pgg.ERR_MISALIGNED
     avg = ctypes.c_double()
     assert L.pgg_moe_fwd_kernel_time(ctypes.byref(d), *args, fake, need, None, 0, ctypes.byref(avg)) == pgg.ERR_INVALID_ARG
+
+
+# ---------------------------------------------------------------- routing
+
+def test_routing_descriptor_checks():
+    L = pgg.lib()
+    n = ctypes.c_size_t()
+    for bad in (dict(batch=0, topk=2, experts=4), dict(batch=4, topk=0, experts=4),
+                dict(batch=4, topk=2, experts=0), dict(batch=4, topk=2, experts=4, x_cols=-1),
+                dict(batch=4, topk=2, experts=4, x_cols=8, x_dtype=7)):
+        d = pgg.make_routing_desc(**bad)
+        assert L.pgg_moe_routing_workspace_size(ctypes.byref(d), ctypes.byref(n)) == pgg.ERR_INVALID_ARG
+    d = pgg.make_routing_desc(4, 2, 9000)
+    assert L.pgg_moe_routing_workspace_size(ctypes.byref(d), ctypes.byref(n)) == pgg.ERR_UNSUPPORTED
+    d = pgg.make_routing_desc(13824, 8, 60, 7168, F16)
+    assert L.pgg_moe_routing_workspace_size(ctypes.byref(d), ctypes.byref(n)) == pgg.OK
+    M = 13824 * 8
+    assert n.value < 4 * M + 8 * 61 + (M // 1024 + 1) * (4 * 60 + 8) + 5 * 512
+    fake = 0x100000
+    assert L.pgg_moe_routing(ctypes.byref(d), None, fake, fake, fake, fake, fake, fake, n.value, None) == pgg.ERR_INVALID_ARG
+    assert L.pgg_moe_routing(ctypes.byref(d), fake, fake, fake, fake, fake, fake, fake, n.value - 1, None) == pgg.ERR_WORKSPACE_TOO_SMALL
+    assert L.pgg_moe_routing(ctypes.byref(d), fake, fake, fake, fake, fake, fake, fake + 8, n.value, None) == pgg.ERR_MISALIGNED
+    assert L.pgg_moe_routing(ctypes.byref(d), fake + 4, fake, fake, fake, fake, fake, fake, n.value, None) == pgg.ERR_MISALIGNED
+    nox = pgg.make_routing_desc(13824, 8, 60)
+    # expanded_x requested without x columns
+    assert L.pgg_moe_routing(ctypes.byref(nox), fake, fake, fake, fake, fake, fake, fake, n.value, None) == pgg.ERR_INVALID_ARG
