@@ -20,9 +20,10 @@ launch's dispatch latency to every measurement.  The CPU baseline is the oracle 
 workload, timed on this host.
 
 Each workload also reports the layer's forward (Permute + GroupedMatmul,
-pgg_moe_fwd) under "forward" and its weight gradient (pgg_moe_dw) under
-"dweight", on the workload's routing, weights and d_y (--no-forward skips
-both); the headline value stays the fused backward's.
+pgg_moe_fwd) under "forward", its weight gradient (pgg_moe_dw) under
+"dweight" and on-device routing (pgg_moe_routing) under "routing", on the
+workload's routing, weights and d_y (--no-forward skips them); the headline
+value stays the fused backward's.
 """
 from __future__ import annotations
 
@@ -227,6 +228,55 @@ def measure_dw(case, gy, eri, gl, steps, log):
                     "preparation and the kernel"}
 
 
+def measure_routing(case, steps, log):
+    """MoeInitRouting on the device (pgg_moe_routing) for the workload's router
+    choices: the tables alone, and with the permuted copy of x."""
+    import numpy as np
+    import torch
+
+    import permute_grouped_gemm_amd as pgg
+    import synth
+
+    dev = torch.device("cuda:0")
+    ids = torch.from_numpy(np.ascontiguousarray(case.expert, dtype=np.int64)).to(dev)
+    x = synth.forward_input(case)
+    if case.dtype == "bf16":
+        xt = torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+    else:
+        xt = torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+    ws = torch.empty(pgg.routing_workspace_size_desc(
+        pgg.make_routing_desc(case.batch, case.topk, case.G, case.K, pgg.DTYPE_CODE[xt.dtype])),
+        dtype=torch.uint8, device=dev)
+    res = {}
+    for label, xin in (("tables_only", None), ("with_expanded_x", xt)):
+        def step():
+            pgg.moe_routing(ids, case.G, xin, workspace=ws)
+        for _ in range(5):
+            step()
+        torch.cuda.synchronize()
+        # GPU time of the call's launches (events around them on its stream);
+        # at the decode size a call's host-side work exceeds its GPU time
+        with pgg.KernelTimer(capacity=steps + 4) as timer:
+            for _ in range(steps):
+                step()
+            torch.cuda.synchronize()
+        n, tot = timer.result["routing"]
+        res[label + "_us"] = tot / n * 1e3
+    code, _ = pgg.read_device_error(ws)
+    if code != 0:
+        raise RuntimeError(f"routing device error {code}")
+    s = {"f32": 4, "f16": 2, "bf16": 2}[case.dtype]
+    moved = case.batch * case.K * s + case.M * case.K * s + 8 * case.M * 3 + 8 * case.G
+    res["expanded_x_bytes"] = case.M * case.K * s
+    res["gbs_with_expanded_x"] = moved / (res["with_expanded_x_us"] * 1e-6) / 1e9
+    res["what"] = ("group_list + both index encodings from expert_ids [batch, topK]; then also "
+                   "expanded_x [M, K] gathered from x; GPU time per call, from HIP events "
+                   "around the call's launches")
+    log(f"[bench] {case.name} routing: tables {res['tables_only_us']:.1f} us, with expanded_x "
+        f"{res['with_expanded_x_us']:.1f} us ({res['gbs_with_expanded_x']:.0f} GB/s)")
+    return res
+
+
 def measure(name, steps, warmup, cpu_baseline, log, forward=True):
     import numpy as np
     import torch
@@ -371,6 +421,7 @@ def measure(name, steps, warmup, cpu_baseline, log, forward=True):
     if forward:
         res["forward"] = measure_forward(case, w, eri, gl, steps, log)
         res["dweight"] = measure_dw(case, gy, eri, gl, steps, log)
+        res["routing"] = measure_routing(case, steps, log)
     if cpu_baseline:
         res["cpu_baseline"] = oracle_baseline(case, unit, log)
     return res
@@ -511,7 +562,7 @@ def main():
     ap.add_argument("--no-large", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-forward", action="store_true",
-                    help="skip the forward and weight-gradient measurements")
+                    help="skip the forward, weight-gradient and routing measurements")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--vendor-gemm", action="store_true",
@@ -554,7 +605,7 @@ def main():
                                               "kernels_event_bracketed_ms_per_step",
                                               "workspace_bytes", "ring_bytes",
                                               "d_expanded_x_fp32_bytes", "plan")}
-    for k in ("forward", "dweight"):
+    for k in ("forward", "dweight", "routing"):
         if k in primary:
             line[k] = primary[k]
     if not args.no_large and args.workload != "large_f16":
@@ -568,7 +619,7 @@ def main():
                                                "d_expanded_x_fp32_bytes", "config", "dtype")}
         if "cpu_baseline" in large:
             line["large"]["cpu_baseline"] = large["cpu_baseline"]
-        for k in ("forward", "dweight"):
+        for k in ("forward", "dweight", "routing"):
             if k in large:
                 line["large"][k] = large[k]
     print(json.dumps(line), flush=True)

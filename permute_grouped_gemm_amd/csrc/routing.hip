@@ -72,7 +72,19 @@ __global__ __launch_bounds__(kScanThreads) void route_scan_kernel(WsHeader* hdr,
   long long mine = 0;
   for (int g = g0; g < g1; ++g) {
     int64_t run = 0;
-    for (int32_t b = 0; b < nblocks; ++b) {
+    int32_t b = 0;
+    // eight blocks at a time: the loads are independent, so they overlap
+    for (; b + 8 <= nblocks; b += 8) {
+      int32_t v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = table[static_cast<int64_t>(b + u) * G + g];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        table[static_cast<int64_t>(b + u) * G + g] = static_cast<int32_t>(run);
+        run += v[u];
+      }
+    }
+    for (; b < nblocks; ++b) {
       int32_t* c = &table[static_cast<int64_t>(b) * G + g];
       const int32_t v = *c;
       *c = static_cast<int32_t>(run);
@@ -119,7 +131,9 @@ __global__ __launch_bounds__(64) void route_place_kernel(const WsHeader* hdr, co
     run[g] = static_cast<int32_t>(offsets[g]) + table[static_cast<int64_t>(blockIdx.x) * G + g];
   __syncthreads();
   const int64_t p0 = static_cast<int64_t>(blockIdx.x) * kBlockPos;
-  for (int c = 0; c < kBlockPos / 64; ++c) {
+  // chunks of 64 positions up to the last one that holds a position (uniform bound)
+  const int n_chunks = static_cast<int>(min<int64_t>(kBlockPos / 64, (M - p0 + 63) / 64));
+  for (int c = 0; c < n_chunks; ++c) {
     const int64_t p = p0 + c * 64 + lane;
     const int32_t e = p < M ? static_cast<int32_t>(ids[p]) : -1;
     int rank = 0, cnt = 0;
