@@ -17,7 +17,10 @@ Permute, then GroupedMatmul): expanded row i copies token p(i) / topK of x,
 and every expert's rows are multiplied by that expert's weight slice, in
 float64, with numpy's matmul as the per-expert product.  ``moe_dw`` is the
 weight gradient the page leaves to a separate operator (§1.2):
-expanded_x^T · d_y per expert, the same way.
+expanded_x^T · d_y per expert, the same way.  ``moe_routing`` builds the
+routing tables from router choices; ``moe_unpermute`` and
+``moe_unpermute_grad`` are the TileLang-Ascend operator page's weighted
+unpermute and its gradient.
 
 Parity status: every function here is pinned by the CPU tests in
 ``tests/test_oracle_*.py`` (brute force, library matmul special cases, the
@@ -340,6 +343,58 @@ def moe_routing(expert_ids, G):
         type0[row] = p
         type1[p] = row
     return np.array(counts, dtype=np.int64), type0, type1
+
+
+def _rows_of_positions(eri, row_idx_type):
+    """inv[p]: the expanded row of original position p (validated permutation)."""
+    _, inv = index(eri, row_idx_type)
+    return inv
+
+
+def moe_unpermute(permuted, eri, row_idx_type, batch, topk, dtype, probs=None):
+    """MoeTokenUnpermute in float64 (TileLang-Ascend operator page, section 4).
+
+    permuted [M, H] (expert outputs in expanded-row order), eri / row_idx_type
+    as for moe_dx, probs [batch, topK] or None, all in the storage type
+    ``dtype``.  With probs: out[t] = sum_j probs[t, j] * permuted[row(t, j)]
+    ([batch, H]), row(t, j) the expanded row of position t*topK + j, summed in
+    slot order.  Without: the gather out[p] = permuted[row(p)] ([M, H]).
+    """
+    M = batch * topk
+    inv = _rows_of_positions(eri, row_idx_type)
+    rows = decode(np.ascontiguousarray(permuted)[inv], dtype)      # row of each position, [M, H]
+    if probs is None:
+        return rows
+    pr = decode(np.ascontiguousarray(probs), dtype).reshape(batch, topk)
+    out = np.zeros((batch, rows.shape[1]), dtype=np.float64)
+    for j in range(topk):
+        out += pr[:, j:j + 1] * rows[j::topk]
+    return out
+
+
+def moe_unpermute_grad(grad_out, eri, row_idx_type, batch, topk, dtype, permuted=None, probs=None):
+    """MoeTokenUnpermuteGrad in float64 (TileLang-Ascend operator page, section 5).
+
+    With probs (and permuted): perm_grad[row(t, j)] = grad_out[t] * probs[t, j]
+    ([M, H]) and probs_grad[t, j] = sum_h grad_out[t, h] * permuted[row(t, j), h]
+    ([batch, topK]); returns (perm_grad, probs_grad).  Without probs, the
+    forward is the gather above and its gradient the scatter
+    perm_grad[row(p)] = grad_out[p] (grad_out [M, H]); returns (perm_grad, None).
+    """
+    M = batch * topk
+    inv = _rows_of_positions(eri, row_idx_type)
+    g = decode(np.ascontiguousarray(grad_out), dtype)
+    perm_grad = np.zeros((M, g.shape[1]), dtype=np.float64)
+    if probs is None:
+        perm_grad[inv] = g
+        return perm_grad, None
+    pr = decode(np.ascontiguousarray(probs), dtype).reshape(batch, topk)
+    rows = decode(np.ascontiguousarray(permuted)[inv], dtype)
+    probs_grad = np.zeros((batch, topk), dtype=np.float64)
+    for j in range(topk):
+        perm_grad[inv[j::topk]] = g * pr[:, j:j + 1]
+        probs_grad[:, j] = np.sum(g * rows[j::topk], axis=1)
+    return perm_grad, probs_grad
 
 
 def case_fwd(case, x, **kw):
