@@ -123,7 +123,7 @@ pgg_status pgg_moe_dx(const pgg_moe_dx_desc* desc, const void* grad_y, const voi
 
 /*
  * Read the device error word of the last pgg_moe_dx (or pgg_moe_fwd,
- * pgg_moe_dw, pgg_moe_routing) that used `workspace`.
+ * pgg_moe_dw, pgg_moe_routing, pgg_moe_unpermute[_grad]) that used `workspace`.
  * Synchronises `stream`.  *code receives a pgg_device_error; *detail its
  * detail value (may be NULL).  When several violations exist, the one with
  * the smallest (code, detail) is reported, so the report is deterministic.
@@ -351,6 +351,46 @@ pgg_status pgg_moe_routing(const pgg_moe_routing_desc* desc, const int64_t* expe
                            const void* x, int64_t* group_list, int64_t* eri_gather,
                            int64_t* eri_scatter, void* expanded_x, void* workspace,
                            size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Unpermute and its gradient (TileLang-Ascend operator page, sections 4 and 5:
+ * MoeTokenUnpermute, MoeTokenUnpermuteGrad), on this library's routing index
+ * (expanded_row_idx and row_idx_type as for pgg_moe_dx); row(t, j) is the
+ * expanded row of original position t*topk + j.  Values are widened to fp32,
+ * multiplied and summed in fp32, and rounded once (round to nearest even) to
+ * `dtype`, the type of every value tensor (probs included).
+ *
+ * With probs (non-NULL, [batch, topk]):
+ *   pgg_moe_unpermute:       out [batch, H] = sum_j probs[t, j] * permuted[row(t, j)]   (slot order)
+ *   pgg_moe_unpermute_grad:  perm_grad [M, H]: perm_grad[row(t, j)] = grad[t] * probs[t, j]
+ *                            probs_grad [batch, topk] = sum_h grad[t, h] * permuted[row(t, j), h]
+ *                            (grad is [batch, H]; a fixed summation order)
+ * Without probs (NULL): the forward is the gather out [M, H], out[p] =
+ * permuted[row(p)], and its gradient the scatter perm_grad[row(p)] = grad[p]
+ * (grad [M, H]; permuted and probs_grad unused).
+ *
+ * Every output element is written.  The routing index is checked on the
+ * device (out of range / not a permutation: the workspace error word, read
+ * with pgg_moe_dx_read_device_error; outputs unspecified).  Value pointers
+ * aligned to the element size, workspace 256-byte aligned.
+ */
+typedef struct {
+  int64_t batch, topk;
+  int64_t hidden;          /* H */
+  int32_t row_idx_type;
+  int32_t dtype;           /* pgg_dtype of permuted, probs, grad and the outputs */
+  int32_t reserved;        /* must be 0 */
+  int32_t pad;
+} pgg_moe_unpermute_desc;
+
+pgg_status pgg_moe_unpermute_workspace_size(const pgg_moe_unpermute_desc* desc, size_t* bytes);
+pgg_status pgg_moe_unpermute(const pgg_moe_unpermute_desc* desc, const void* permuted,
+                             const int64_t* expanded_row_idx, const void* probs, void* out,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+pgg_status pgg_moe_unpermute_grad(const pgg_moe_unpermute_desc* desc, const void* permuted,
+                                  const void* grad, const int64_t* expanded_row_idx,
+                                  const void* probs, void* perm_grad, void* probs_grad,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 const char* pgg_status_string(pgg_status status);
 const char* pgg_device_error_string(int32_t code);

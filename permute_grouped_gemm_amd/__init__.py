@@ -40,7 +40,8 @@ import torch
 __all__ = [
     "moe_dx", "workspace_size", "plan", "read_device_error", "debug_tables", "debug_tiles",
     "moe_fwd", "fwd_workspace_size", "fwd_plan", "fwd_kernel_time",
-    "moe_dw", "dw_workspace_size", "dw_kernel_time", "moe_routing",
+    "moe_dw", "dw_workspace_size", "dw_kernel_time", "moe_routing", "moe_unpermute",
+    "moe_unpermute_grad",
     "KernelTimer", "PggError", "lib", "LIB_PATH", "HEADER_PATH",
 ]
 
@@ -79,6 +80,14 @@ class RoutingDesc(ctypes.Structure):
     _fields_ = [
         ("batch", ctypes.c_int64), ("topk", ctypes.c_int64), ("experts", ctypes.c_int64),
         ("x_cols", ctypes.c_int64), ("x_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
+    ]
+
+
+class UnpermuteDesc(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int64), ("topk", ctypes.c_int64), ("hidden", ctypes.c_int64),
+        ("row_idx_type", ctypes.c_int32), ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("pad", ctypes.c_int32),
     ]
 
 
@@ -141,6 +150,10 @@ def lib():
         PR = ctypes.POINTER(RoutingDesc)
         L.pgg_moe_routing_workspace_size.argtypes = [PR, ctypes.POINTER(sz)]
         L.pgg_moe_routing.argtypes = [PR, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        PU = ctypes.POINTER(UnpermuteDesc)
+        L.pgg_moe_unpermute_workspace_size.argtypes = [PU, ctypes.POINTER(sz)]
+        L.pgg_moe_unpermute.argtypes = [PU, vp, vp, vp, vp, vp, sz, vp]
+        L.pgg_moe_unpermute_grad.argtypes = [PU, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.pgg_timing_begin.argtypes = [i32]
         L.pgg_timing_end.argtypes = [ctypes.POINTER(KernelTime), i32, ctypes.POINTER(i32)]
         L.pgg_status_string.argtypes = [ctypes.c_int]
@@ -152,7 +165,8 @@ def lib():
                   "pgg_moe_dx_kernel_time", "pgg_moe_fwd_workspace_size", "pgg_moe_fwd",
                   "pgg_moe_fwd_plan", "pgg_moe_fwd_kernel_time", "pgg_moe_dw_workspace_size",
                   "pgg_moe_dw", "pgg_moe_dw_kernel_time", "pgg_moe_routing_workspace_size",
-                  "pgg_moe_routing",
+                  "pgg_moe_routing", "pgg_moe_unpermute_workspace_size", "pgg_moe_unpermute",
+                  "pgg_moe_unpermute_grad",
                   "pgg_timing_begin", "pgg_timing_end"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
@@ -530,6 +544,63 @@ def moe_routing(expert_ids: torch.Tensor, experts: int, x: Optional[torch.Tensor
                                workspace.numel() * workspace.element_size(), _stream_handle(stream))
     _check(st, "pgg_moe_routing")
     return gl, eg, es, ex
+
+
+# ---------------------------------------------------------------- unpermute
+
+def make_unpermute_desc(batch, topk, hidden, row_idx_type, dtype) -> UnpermuteDesc:
+    d = UnpermuteDesc()
+    d.batch, d.topk, d.hidden = int(batch), int(topk), int(hidden)
+    d.row_idx_type, d.dtype, d.reserved, d.pad = int(row_idx_type), int(dtype), 0, 0
+    return d
+
+
+def _unpermute_ws(d, dev, workspace):
+    if workspace is not None:
+        return workspace
+    n = ctypes.c_size_t()
+    _check(lib().pgg_moe_unpermute_workspace_size(ctypes.byref(d), ctypes.byref(n)),
+           "unpermute_workspace_size")
+    return torch.empty(n.value, dtype=torch.uint8, device=dev)
+
+
+def moe_unpermute(permuted: torch.Tensor, expanded_row_idx: torch.Tensor, batch: int, topk: int,
+                  row_idx_type: int = 0, probs: Optional[torch.Tensor] = None, *, workspace=None,
+                  stream=None) -> torch.Tensor:
+    """MoeTokenUnpermute: with probs [batch, topk], out [batch, H] = sum over
+    slots of probs * the token's expert rows; without, the gather [M, H].
+    permuted [batch*topk, H]; results in permuted's dtype (fp32 arithmetic)."""
+    H = permuted.shape[1]
+    d = make_unpermute_desc(batch, topk, H, row_idx_type, DTYPE_CODE.get(permuted.dtype, -1))
+    shape = (int(batch), H) if probs is not None else (int(batch) * int(topk), H)
+    out = torch.empty(shape, dtype=permuted.dtype, device=permuted.device)
+    ws = _unpermute_ws(d, permuted.device, workspace)
+    st = lib().pgg_moe_unpermute(ctypes.byref(d), permuted.data_ptr(), expanded_row_idx.data_ptr(),
+                                 None if probs is None else probs.data_ptr(), out.data_ptr(),
+                                 ws.data_ptr(), ws.numel(), _stream_handle(stream))
+    _check(st, "pgg_moe_unpermute")
+    return out
+
+
+def moe_unpermute_grad(grad: torch.Tensor, expanded_row_idx: torch.Tensor, batch: int, topk: int,
+                       row_idx_type: int = 0, permuted: Optional[torch.Tensor] = None,
+                       probs: Optional[torch.Tensor] = None, *, workspace=None, stream=None):
+    """MoeTokenUnpermuteGrad: (perm_grad [M, H], probs_grad [batch, topk] or
+    None).  With probs, grad is [batch, H] and permuted is needed; without,
+    grad is [M, H] and perm_grad its scatter back to expanded rows."""
+    H = grad.shape[1]
+    d = make_unpermute_desc(batch, topk, H, row_idx_type, DTYPE_CODE.get(grad.dtype, -1))
+    M = int(batch) * int(topk)
+    perm_grad = torch.empty((M, H), dtype=grad.dtype, device=grad.device)
+    probs_grad = (torch.empty((int(batch), int(topk)), dtype=grad.dtype, device=grad.device)
+                  if probs is not None else None)
+    ws = _unpermute_ws(d, grad.device, workspace)
+    ptr = lambda t: None if t is None else t.data_ptr()
+    st = lib().pgg_moe_unpermute_grad(ctypes.byref(d), ptr(permuted), grad.data_ptr(),
+                                      expanded_row_idx.data_ptr(), ptr(probs), perm_grad.data_ptr(),
+                                      ptr(probs_grad), ws.data_ptr(), ws.numel(), _stream_handle(stream))
+    _check(st, "pgg_moe_unpermute_grad")
+    return perm_grad, probs_grad
 
 
 class KernelTimer:

@@ -17,7 +17,8 @@ OUT = os.path.join(PKG, "libpgg.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 SOURCES = ["plan.cpp", "api.cpp", "prep.hip", "gemm.hip", "gemm_large.hip", "gemm_sweep.hip", "consume.hip",
            "fwd.hip", "fwd_large.hip", "dw.hip",
-           "dw_large.hip", "routing.hip"]
+           "dw_large.hip", "routing.hip",
+           "unpermute.hip"]
 ARCH = os.environ.get("PGG_ARCH", "gfx950")
 
 FLAGS = [

@@ -1,5 +1,6 @@
 // C ABI of the fused MoE d_x backward, of the layer's forward, of its weight
-// gradient and of on-device routing (declared in include/pgg.h).
+// gradient, of on-device routing and of unpermute and its gradient (declared
+// in include/pgg.h).
 //
 // The execute call validates the descriptor on the host, lays out the
 // workspace, and enqueues on the caller's stream:
@@ -433,6 +434,65 @@ pgg_status pgg_moe_routing(const pgg_moe_routing_desc* desc, const int64_t* expe
     TimedLaunch t("routing", stream);
     e = launch_routing(p, expert_ids, x, group_list, eri_gather, eri_scatter, expanded_x, workspace,
                        vec, stream);
+  }
+  return e == hipSuccess ? PGG_OK : PGG_ERR_HIP;
+}
+
+pgg_status pgg_moe_unpermute_workspace_size(const pgg_moe_unpermute_desc* desc, size_t* bytes) {
+  if (!bytes) return PGG_ERR_INVALID_ARG;
+  UnpermutePlan p;
+  const pgg_status st = make_unpermute_plan(desc, &p);
+  if (st != PGG_OK) return st;
+  *bytes = p.total;
+  return PGG_OK;
+}
+
+static pgg_status check_unpermute(const pgg_moe_unpermute_desc* desc, const void* const* values,
+                                  int n_values, const int64_t* eri, void* workspace,
+                                  size_t workspace_bytes, UnpermutePlan* p) {
+  const pgg_status st = make_unpermute_plan(desc, p);
+  if (st != PGG_OK) return st;
+  if (!eri || !workspace) return PGG_ERR_INVALID_ARG;
+  if (workspace_bytes < p->total) return PGG_ERR_WORKSPACE_TOO_SMALL;
+  if (!is_aligned(workspace, kWorkspaceAlign) || !is_aligned(eri, 8)) return PGG_ERR_MISALIGNED;
+  for (int i = 0; i < n_values; ++i) {
+    if (!values[i]) return PGG_ERR_INVALID_ARG;
+    if (!is_aligned(values[i], elem_size(p->dtype))) return PGG_ERR_MISALIGNED;
+  }
+  return PGG_OK;
+}
+
+pgg_status pgg_moe_unpermute(const pgg_moe_unpermute_desc* desc, const void* permuted,
+                             const int64_t* expanded_row_idx, const void* probs, void* out,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  UnpermutePlan p;
+  const void* vals[3] = {permuted, out, probs};
+  const pgg_status st = check_unpermute(desc, vals, probs ? 3 : 2, expanded_row_idx, workspace,
+                                        workspace_bytes, &p);
+  if (st != PGG_OK) return st;
+  hipError_t e;
+  {
+    TimedLaunch t("unpermute", stream);
+    e = launch_unpermute(p, workspace, expanded_row_idx, permuted, nullptr, probs, out, nullptr, false,
+                         stream);
+  }
+  return e == hipSuccess ? PGG_OK : PGG_ERR_HIP;
+}
+
+pgg_status pgg_moe_unpermute_grad(const pgg_moe_unpermute_desc* desc, const void* permuted,
+                                  const void* grad, const int64_t* expanded_row_idx,
+                                  const void* probs, void* perm_grad, void* probs_grad,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  UnpermutePlan p;
+  const void* with[5] = {grad, perm_grad, probs, permuted, probs_grad};
+  const pgg_status st = check_unpermute(desc, with, probs ? 5 : 2, expanded_row_idx, workspace,
+                                        workspace_bytes, &p);
+  if (st != PGG_OK) return st;
+  hipError_t e;
+  {
+    TimedLaunch t("unpermute_grad", stream);
+    e = launch_unpermute(p, workspace, expanded_row_idx, permuted, grad, probs, perm_grad, probs_grad,
+                         true, stream);
   }
   return e == hipSuccess ? PGG_OK : PGG_ERR_HIP;
 }

@@ -130,6 +130,17 @@ hipError_t launch_consume(const Plan& p, int chunk, const WsView& w, float* grad
 
 const char* produce_kernel_name(const Plan& p);
 
+// Unpermute and its gradient: workspace layout and launches.
+struct UnpermutePlan {
+  int64_t M, batch, topk, H;
+  int32_t dtype, row_idx_type;
+  size_t off_header, off_inv, off_ori, total;
+};
+pgg_status make_unpermute_plan(const pgg_moe_unpermute_desc* desc, UnpermutePlan* plan);
+hipError_t launch_unpermute(const UnpermutePlan& p, void* ws, const int64_t* eri, const void* permuted,
+                            const void* grad, const void* probs, void* out, void* probs_grad,
+                            bool is_grad, hipStream_t s);
+
 // MoeInitRouting on the device: workspace layout and launches.
 struct RoutePlan {
   int64_t M, G, topk, K;

@@ -220,6 +220,32 @@ pgg_status make_routing_plan(const pgg_moe_routing_desc* d, RoutePlan* p) {
   return PGG_OK;
 }
 
+pgg_status make_unpermute_plan(const pgg_moe_unpermute_desc* d, UnpermutePlan* p) {
+  if (!d || !p) return PGG_ERR_INVALID_ARG;
+  if (d->reserved != 0 || d->batch <= 0 || d->topk <= 0 || d->hidden <= 0) return PGG_ERR_INVALID_ARG;
+  if (d->row_idx_type != 0 && d->row_idx_type != 1) return PGG_ERR_INVALID_ARG;
+  if (d->dtype < PGG_F32 || d->dtype > PGG_BF16) return PGG_ERR_INVALID_ARG;
+  if (d->topk > INT64_MAX / d->batch) return PGG_ERR_INVALID_ARG;
+  const int64_t M = d->batch * d->topk;
+  if (M >= (int64_t(1) << 31) - 1 || d->batch >= (int64_t(1) << 31) ||
+      d->hidden >= (int64_t(1) << 40) / M)
+    return PGG_ERR_UNSUPPORTED;
+  UnpermutePlan q{};
+  q.M = M;
+  q.batch = d->batch;
+  q.topk = d->topk;
+  q.H = d->hidden;
+  q.dtype = d->dtype;
+  q.row_idx_type = d->row_idx_type;
+  size_t off = 0;
+  q.off_header = off; off = align_up(off + sizeof(WsHeader), kRegionAlign);
+  q.off_inv = off;    off = align_up(off + sizeof(int32_t) * size_t(M), kRegionAlign);
+  q.off_ori = off;    off = align_up(off + sizeof(int32_t) * size_t(M), kRegionAlign);
+  q.total = off;
+  *p = q;
+  return PGG_OK;
+}
+
 pgg_status make_dw_plan(const pgg_moe_fwd_desc* d, Plan* p) {
   Plan q;
   const pgg_status st = make_fwd_plan(d, &q);

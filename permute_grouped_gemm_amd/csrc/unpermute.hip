@@ -1,0 +1,190 @@
+// Unpermute and its gradient (TileLang-Ascend operator page, sections 4 and 5:
+// MoeTokenUnpermute, MoeTokenUnpermuteGrad), on the routing tables of the
+// other operators:
+//
+//   with probabilities:  out[t]            = sum_j probs[t, j] * permuted[row(t, j)]      [batch, H]
+//                        perm_grad[row(t,j)] = grad[t] * probs[t, j]                      [M, H]
+//                        probs_grad[t, j]  = sum_h grad[t, h] * permuted[row(t, j), h]   [batch, topK]
+//   without:             out[p] = permuted[row(p)],  perm_grad[row(p)] = grad[p]           [M, H]
+//
+// row(t, j) is the expanded row of original position t*topK + j.  Values are
+// widened to fp32, multiplied and summed in fp32 (slot order for out; a fixed
+// tree over h for probs_grad) and rounded once to the tensors' type, so every
+// result is independent of timing.  The routing index is inverted and checked
+// first by the shared index-preparation kernels.
+#include <algorithm>
+
+#include "pgg_device.h"
+
+namespace pgg {
+
+namespace {
+
+template <class T> __device__ __forceinline__ float ld(const void* p, int64_t i);
+template <> __device__ __forceinline__ float ld<TF32>(const void* p, int64_t i) {
+  return static_cast<const float*>(p)[i];
+}
+template <> __device__ __forceinline__ float ld<TF16>(const void* p, int64_t i) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<const uint16_t*>(p)[i]));
+}
+template <> __device__ __forceinline__ float ld<TBf16>(const void* p, int64_t i) {
+  return __builtin_bit_cast(float, static_cast<uint32_t>(static_cast<const uint16_t*>(p)[i]) << 16);
+}
+
+template <class T> __device__ __forceinline__ void st(void* p, int64_t i, float v);
+template <> __device__ __forceinline__ void st<TF32>(void* p, int64_t i, float v) {
+  static_cast<float*>(p)[i] = v;
+}
+template <> __device__ __forceinline__ void st<TF16>(void* p, int64_t i, float v) {
+  static_cast<uint16_t*>(p)[i] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(v));   // RNE
+}
+template <> __device__ __forceinline__ void st<TBf16>(void* p, int64_t i, float v) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  uint16_t r;
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu))
+    r = 0x7FC0;                                               // NaN stays NaN
+  else
+    r = static_cast<uint16_t>((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);   // round to nearest even
+  static_cast<uint16_t*>(p)[i] = r;
+}
+
+__global__ void unpermute_reset_kernel(WsHeader* hdr) {
+  hdr->err = kNoError;
+  hdr->n_tiles = 0;
+}
+
+constexpr int kThreads = 256;
+constexpr int kPerThread = 4;
+constexpr int kCols = kThreads * kPerThread;    // columns per workgroup
+
+// out[t, h] = sum_j probs[t, j] * permuted[inv[t*topK + j], h]; grid (batch, column blocks)
+template <class T>
+__global__ __launch_bounds__(kThreads) void unpermute_kernel(const WsHeader* hdr, const int32_t* inv,
+                                                             const void* permuted, const void* probs,
+                                                             void* out, int64_t H, int64_t topk) {
+  if (hdr->err != kNoError) return;
+  const int64_t t = blockIdx.x;
+  const int64_t h0 = static_cast<int64_t>(blockIdx.y) * kCols + threadIdx.x;
+  float acc[kPerThread];
+#pragma unroll
+  for (int k = 0; k < kPerThread; ++k) acc[k] = 0.0f;
+  for (int64_t j = 0; j < topk; ++j) {
+    const int64_t r = inv[t * topk + j];
+    const float pj = ld<T>(probs, t * topk + j);
+#pragma unroll
+    for (int k = 0; k < kPerThread; ++k) {
+      const int64_t h = h0 + k * kThreads;
+      if (h < H) acc[k] += pj * ld<T>(permuted, r * H + h);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < kPerThread; ++k) {
+    const int64_t h = h0 + k * kThreads;
+    if (h < H) st<T>(out, t * H + h, acc[k]);
+  }
+}
+
+// Row copies: dst[drow(p)] = src[srow(p)] for every position p; grid (M, column blocks).
+// gather: drow = p, srow = inv[p]; scatter: drow = inv[p], srow = p.
+__global__ __launch_bounds__(kThreads) void permute_rows_kernel(const WsHeader* hdr,
+                                                                const int32_t* inv,
+                                                                const uint16_t* src, uint16_t* dst,
+                                                                int64_t row_halves, int32_t scatter) {
+  if (hdr->err != kNoError) return;
+  const int64_t p = blockIdx.x;
+  const int64_t r = inv[p];
+  const uint16_t* s = src + (scatter ? p : r) * row_halves;
+  uint16_t* d = dst + (scatter ? r : p) * row_halves;
+  for (int64_t b = static_cast<int64_t>(blockIdx.y) * kThreads + threadIdx.x; b < row_halves;
+       b += static_cast<int64_t>(gridDim.y) * kThreads)
+    d[b] = s[b];
+}
+
+// One workgroup per token: for every slot j, perm_grad[row] = grad[t] * p and
+// probs_grad[t, j] = sum_h grad[t, h] * permuted[row, h] (per-thread sums over
+// a fixed set of h, a fixed butterfly within each wave, then the waves in order).
+template <class T>
+__global__ __launch_bounds__(kThreads) void unpermute_grad_kernel(
+    const WsHeader* hdr, const int32_t* inv, const void* permuted, const void* grad,
+    const void* probs, void* perm_grad, void* probs_grad, int64_t H, int64_t topk) {
+  __shared__ float s_wave[kThreads / 64];
+  if (hdr->err != kNoError) return;
+  const int64_t t = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int64_t j = 0; j < topk; ++j) {
+    const int64_t r = inv[t * topk + j];
+    const float pj = ld<T>(probs, t * topk + j);
+    float part = 0.0f;
+    for (int64_t h = threadIdx.x; h < H; h += kThreads) {
+      const float g = ld<T>(grad, t * H + h);
+      st<T>(perm_grad, r * H + h, g * pj);
+      part += g * ld<T>(permuted, r * H + h);
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) part += __shfl_xor(part, m);
+    if (lane == 0) s_wave[wave] = part;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      float sum = s_wave[0];
+#pragma unroll
+      for (int w = 1; w < kThreads / 64; ++w) sum += s_wave[w];
+      st<T>(probs_grad, t * topk + j, sum);
+    }
+    __syncthreads();
+  }
+}
+
+template <class T>
+hipError_t launch_typed(const UnpermutePlan& p, const int32_t* inv, const void* a, const void* b,
+                        const void* probs, void* o1, void* o2, bool grad, hipStream_t s,
+                        const WsHeader* hdr) {
+  if (!grad) {
+    const dim3 grid(static_cast<unsigned>(p.batch), static_cast<unsigned>((p.H + kCols - 1) / kCols));
+    hipLaunchKernelGGL(unpermute_kernel<T>, grid, dim3(kThreads), 0, s, hdr, inv, a, probs, o1, p.H,
+                       p.topk);
+  } else {
+    hipLaunchKernelGGL(unpermute_grad_kernel<T>, dim3(static_cast<unsigned>(p.batch)), dim3(kThreads),
+                       0, s, hdr, inv, a, b, probs, o1, o2, p.H, p.topk);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_unpermute(const UnpermutePlan& p, void* ws, const int64_t* eri, const void* permuted,
+                            const void* grad, const void* probs, void* out, void* probs_grad,
+                            bool is_grad, hipStream_t s) {
+  char* base = static_cast<char*>(ws);
+  WsHeader* hdr = reinterpret_cast<WsHeader*>(base + p.off_header);
+  Plan q{};
+  q.M = p.M;
+  q.topk = p.topk;
+  q.row_idx_type = p.row_idx_type;
+  WsView w{};
+  w.hdr = hdr;
+  w.inv = reinterpret_cast<int32_t*>(base + p.off_inv);
+  w.ori = reinterpret_cast<int32_t*>(base + p.off_ori);
+  hipLaunchKernelGGL(unpermute_reset_kernel, dim3(1), dim3(1), 0, s, hdr);
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess) e = launch_prep_index(q, eri, w, s);
+  if (e == hipSuccess) e = launch_prep_verify(q, eri, w, s);
+  if (e != hipSuccess) return e;
+  if (!probs) {
+    // gather (forward) or scatter (gradient) of whole rows
+    // rows copied in 2-byte units (every element type is a whole number of them)
+    const int64_t row_halves = p.H * (p.dtype == PGG_F32 ? 2 : 1);
+    const unsigned yblocks =
+        static_cast<unsigned>(std::min<int64_t>((row_halves + kThreads - 1) / kThreads, 16));
+    const uint16_t* src = static_cast<const uint16_t*>(is_grad ? grad : permuted);
+    hipLaunchKernelGGL(permute_rows_kernel, dim3(static_cast<unsigned>(p.M), yblocks), dim3(kThreads), 0,
+                       s, hdr, w.inv, src, static_cast<uint16_t*>(out), row_halves, is_grad ? 1 : 0);
+    return hipGetLastError();
+  }
+  if (p.dtype == PGG_F32)
+    return launch_typed<TF32>(p, w.inv, permuted, grad, probs, out, probs_grad, is_grad, s, hdr);
+  if (p.dtype == PGG_BF16)
+    return launch_typed<TBf16>(p, w.inv, permuted, grad, probs, out, probs_grad, is_grad, s, hdr);
+  return launch_typed<TF16>(p, w.inv, permuted, grad, probs, out, probs_grad, is_grad, s, hdr);
+}
+
+}  // namespace pgg

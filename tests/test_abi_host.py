@@ -208,3 +208,26 @@ def test_routing_descriptor_checks():
     nox = pgg.make_routing_desc(13824, 8, 60)
     # expanded_x requested without x columns
     assert L.pgg_moe_routing(ctypes.byref(nox), fake, fake, fake, fake, fake, fake, fake, n.value, None) == pgg.ERR_INVALID_ARG
+
+
+# ---------------------------------------------------------------- unpermute
+
+def test_unpermute_descriptor_checks():
+    L = pgg.lib()
+    n = ctypes.c_size_t()
+    for bad in (dict(batch=0, topk=2, hidden=8, row_idx_type=0, dtype=F32),
+                dict(batch=4, topk=0, hidden=8, row_idx_type=0, dtype=F32),
+                dict(batch=4, topk=2, hidden=0, row_idx_type=0, dtype=F32),
+                dict(batch=4, topk=2, hidden=8, row_idx_type=2, dtype=F32),
+                dict(batch=4, topk=2, hidden=8, row_idx_type=0, dtype=5)):
+        d = pgg.make_unpermute_desc(**bad)
+        assert L.pgg_moe_unpermute_workspace_size(ctypes.byref(d), ctypes.byref(n)) == pgg.ERR_INVALID_ARG
+    d = pgg.make_unpermute_desc(64, 8, 7168, 0, BF16)
+    assert L.pgg_moe_unpermute_workspace_size(ctypes.byref(d), ctypes.byref(n)) == pgg.OK
+    assert n.value <= 512 + 2 * (4 * 512 + 512)
+    fake = 0x100000
+    assert L.pgg_moe_unpermute(ctypes.byref(d), fake, fake, fake, fake, fake, n.value - 1, None) == pgg.ERR_WORKSPACE_TOO_SMALL
+    assert L.pgg_moe_unpermute(ctypes.byref(d), fake + 1, fake, fake, fake, fake, n.value, None) == pgg.ERR_MISALIGNED
+    assert L.pgg_moe_unpermute(ctypes.byref(d), None, fake, fake, fake, fake, n.value, None) == pgg.ERR_INVALID_ARG
+    # with probabilities the gradient needs permuted and probs_grad
+    assert L.pgg_moe_unpermute_grad(ctypes.byref(d), None, fake, fake, fake, fake, fake, fake, n.value, None) == pgg.ERR_INVALID_ARG
