@@ -21,9 +21,9 @@ workload, timed on this host.
 
 Each workload also reports the layer's forward (Permute + GroupedMatmul,
 pgg_moe_fwd) under "forward", its weight gradient (pgg_moe_dw) under
-"dweight" and on-device routing (pgg_moe_routing) under "routing", on the
-workload's routing, weights and d_y (--no-forward skips them); the headline
-value stays the fused backward's.
+"dweight", on-device routing (pgg_moe_routing) under "routing" and unpermute
+with its gradient under "unpermute", on the workload's routing, weights and
+d_y (--no-forward skips them); the headline value stays the fused backward's.
 """
 from __future__ import annotations
 
@@ -277,6 +277,53 @@ def measure_routing(case, steps, log):
     return res
 
 
+def measure_unpermute(case, eri, steps, log):
+    """Unpermute (weighted topK sum) and its gradient at the workload's routing,
+    with hidden size K and seeded random tokens, probabilities and gradients."""
+    import torch
+
+    import permute_grouped_gemm_amd as pgg
+
+    dev = eri.device
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[case.dtype]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(case.seed + 100)
+    perm = torch.randn((case.M, case.K), generator=gen, device=dev).to(tdt)
+    probs = torch.rand((case.batch, case.topk), generator=gen, device=dev).to(tdt)
+    grad = torch.randn((case.batch, case.K), generator=gen, device=dev).to(tdt)
+    ws = torch.empty(1 << 20, dtype=torch.uint8, device=dev)
+    res = {}
+    calls = {
+        "unpermute": lambda: pgg.moe_unpermute(perm, eri, case.batch, case.topk, case.row_idx_type,
+                                               probs, workspace=ws),
+        "unpermute_grad": lambda: pgg.moe_unpermute_grad(grad, eri, case.batch, case.topk,
+                                                         case.row_idx_type, perm, probs, workspace=ws),
+    }
+    s = {"f32": 4, "f16": 2, "bf16": 2}[case.dtype]
+    moved = {"unpermute": case.M * case.K * s + case.batch * case.K * s,
+             "unpermute_grad": case.batch * case.K * s + 2 * case.M * case.K * s}
+    for name, fn in calls.items():
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        with pgg.KernelTimer(capacity=steps + 4) as timer:
+            for _ in range(steps):
+                fn()
+            torch.cuda.synchronize()
+        n, tot = timer.result[name]
+        us = tot / n * 1e3
+        res[name] = {"us": us, "gbs": moved[name] / (us * 1e-6) / 1e9, "bytes": moved[name]}
+    code, _ = pgg.read_device_error(ws)
+    if code != 0:
+        raise RuntimeError(f"unpermute device error {code}")
+    res["what"] = ("unpermute: out[t] = sum_j probs[t,j] permuted[row(t,j)] ([batch, K], K = hidden); "
+                   "grad: perm_grad and probs_grad; GPU time per call from HIP events around its launches")
+    log(f"[bench] {case.name} unpermute: {res['unpermute']['us']:.1f} us ({res['unpermute']['gbs']:.0f} GB/s), "
+        f"grad {res['unpermute_grad']['us']:.1f} us ({res['unpermute_grad']['gbs']:.0f} GB/s)")
+    del perm, probs, grad
+    return res
+
+
 def measure(name, steps, warmup, cpu_baseline, log, forward=True):
     import numpy as np
     import torch
@@ -422,6 +469,7 @@ def measure(name, steps, warmup, cpu_baseline, log, forward=True):
         res["forward"] = measure_forward(case, w, eri, gl, steps, log)
         res["dweight"] = measure_dw(case, gy, eri, gl, steps, log)
         res["routing"] = measure_routing(case, steps, log)
+        res["unpermute"] = measure_unpermute(case, eri, steps, log)
     if cpu_baseline:
         res["cpu_baseline"] = oracle_baseline(case, unit, log)
     return res
@@ -562,7 +610,7 @@ def main():
     ap.add_argument("--no-large", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-forward", action="store_true",
-                    help="skip the forward, weight-gradient and routing measurements")
+                    help="skip the forward, weight-gradient, routing and unpermute measurements")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--vendor-gemm", action="store_true",
@@ -605,7 +653,7 @@ def main():
                                               "kernels_event_bracketed_ms_per_step",
                                               "workspace_bytes", "ring_bytes",
                                               "d_expanded_x_fp32_bytes", "plan")}
-    for k in ("forward", "dweight", "routing"):
+    for k in ("forward", "dweight", "routing", "unpermute"):
         if k in primary:
             line[k] = primary[k]
     if not args.no_large and args.workload != "large_f16":
@@ -619,7 +667,7 @@ def main():
                                                "d_expanded_x_fp32_bytes", "config", "dtype")}
         if "cpu_baseline" in large:
             line["large"]["cpu_baseline"] = large["cpu_baseline"]
-        for k in ("forward", "dweight", "routing"):
+        for k in ("forward", "dweight", "routing", "unpermute"):
             if k in large:
                 line["large"][k] = large[k]
     print(json.dumps(line), flush=True)

@@ -48,6 +48,46 @@ template <> __device__ __forceinline__ void st<TBf16>(void* p, int64_t i, float 
   static_cast<uint16_t*>(p)[i] = r;
 }
 
+// 16-byte chunks: 16 / sizeof(elem) values widened to fp32 / rounded back.
+template <class T> struct Chunk { static constexpr int N = 16 / int(sizeof(typename T::elem)); };
+
+template <class T>
+__device__ __forceinline__ void ldv(const void* base, int64_t i, float (&v)[Chunk<T>::N]) {
+  const u32x4_t raw = *reinterpret_cast<const u32x4_t*>(static_cast<const typename T::elem*>(base) + i);
+  if constexpr (Chunk<T>::N == 4) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t w = raw[k];   // a scalar copy: bit-casting the vector element lvalue read element 0
+      v[k] = __builtin_bit_cast(float, w);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint16_t lo = static_cast<uint16_t>(raw[k] & 0xFFFFu), hi = static_cast<uint16_t>(raw[k] >> 16);
+      v[2 * k] = ld<T>(&lo, 0);
+      v[2 * k + 1] = ld<T>(&hi, 0);
+    }
+  }
+}
+
+template <class T>
+__device__ __forceinline__ void stv(void* base, int64_t i, const float (&v)[Chunk<T>::N]) {
+  u32x4_t raw;
+  if constexpr (Chunk<T>::N == 4) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) raw[k] = __builtin_bit_cast(uint32_t, v[k]);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      uint16_t lo, hi;
+      st<T>(&lo, 0, v[2 * k]);
+      st<T>(&hi, 0, v[2 * k + 1]);
+      raw[k] = static_cast<uint32_t>(lo) | (static_cast<uint32_t>(hi) << 16);
+    }
+  }
+  *reinterpret_cast<u32x4_t*>(static_cast<typename T::elem*>(base) + i) = raw;
+}
+
 __global__ void unpermute_reset_kernel(WsHeader* hdr) {
   hdr->err = kNoError;
   hdr->n_tiles = 0;
@@ -82,6 +122,33 @@ __global__ __launch_bounds__(kThreads) void unpermute_kernel(const WsHeader* hdr
     const int64_t h = h0 + k * kThreads;
     if (h < H) st<T>(out, t * H + h, acc[k]);
   }
+}
+
+// The same with 16-byte chunks (rows 16-byte aligned): thread = one chunk of
+// the token's row; grid (batch, chunk blocks of kThreads).
+template <class T>
+__global__ __launch_bounds__(kThreads) void unpermute_vec_kernel(const WsHeader* hdr,
+                                                                 const int32_t* inv,
+                                                                 const void* permuted,
+                                                                 const void* probs, void* out,
+                                                                 int64_t H, int64_t topk) {
+  constexpr int N = Chunk<T>::N;
+  if (hdr->err != kNoError) return;
+  const int64_t t = blockIdx.x;
+  const int64_t h = (static_cast<int64_t>(blockIdx.y) * kThreads + threadIdx.x) * N;
+  if (h >= H) return;
+  float acc[N];
+#pragma unroll
+  for (int k = 0; k < N; ++k) acc[k] = 0.0f;
+  for (int64_t j = 0; j < topk; ++j) {
+    const int64_t r = inv[t * topk + j];
+    const float pj = ld<T>(probs, t * topk + j);
+    float v[N];
+    ldv<T>(permuted, r * H + h, v);
+#pragma unroll
+    for (int k = 0; k < N; ++k) acc[k] += pj * v[k];
+  }
+  stv<T>(out, t * H + h, acc);
 }
 
 // Row copies: dst[drow(p)] = src[srow(p)] for every position p; grid (M, column blocks).
@@ -134,14 +201,64 @@ __global__ __launch_bounds__(kThreads) void unpermute_grad_kernel(
   }
 }
 
+// The gradient with 16-byte chunks (rows 16-byte aligned).
+template <class T>
+__global__ __launch_bounds__(kThreads) void unpermute_grad_vec_kernel(
+    const WsHeader* hdr, const int32_t* inv, const void* permuted, const void* grad,
+    const void* probs, void* perm_grad, void* probs_grad, int64_t H, int64_t topk) {
+  constexpr int N = Chunk<T>::N;
+  __shared__ float s_wave[kThreads / 64];
+  if (hdr->err != kNoError) return;
+  const int64_t t = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int64_t j = 0; j < topk; ++j) {
+    const int64_t r = inv[t * topk + j];
+    const float pj = ld<T>(probs, t * topk + j);
+    float part = 0.0f;
+    for (int64_t h = static_cast<int64_t>(threadIdx.x) * N; h < H; h += kThreads * N) {
+      float g[N], x[N], o[N];
+      ldv<T>(grad, t * H + h, g);
+      ldv<T>(permuted, r * H + h, x);
+#pragma unroll
+      for (int k = 0; k < N; ++k) {
+        o[k] = g[k] * pj;
+        part += g[k] * x[k];
+      }
+      stv<T>(perm_grad, r * H + h, o);
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) part += __shfl_xor(part, m);
+    if (lane == 0) s_wave[wave] = part;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      float sum = s_wave[0];
+#pragma unroll
+      for (int w = 1; w < kThreads / 64; ++w) sum += s_wave[w];
+      st<T>(probs_grad, t * topk + j, sum);
+    }
+    __syncthreads();
+  }
+}
+
 template <class T>
 hipError_t launch_typed(const UnpermutePlan& p, const int32_t* inv, const void* a, const void* b,
-                        const void* probs, void* o1, void* o2, bool grad, hipStream_t s,
+                        const void* probs, void* o1, void* o2, bool grad, bool vec, hipStream_t s,
                         const WsHeader* hdr) {
+  constexpr int N = Chunk<T>::N;
   if (!grad) {
-    const dim3 grid(static_cast<unsigned>(p.batch), static_cast<unsigned>((p.H + kCols - 1) / kCols));
-    hipLaunchKernelGGL(unpermute_kernel<T>, grid, dim3(kThreads), 0, s, hdr, inv, a, probs, o1, p.H,
-                       p.topk);
+    if (vec) {
+      const dim3 grid(static_cast<unsigned>(p.batch),
+                      static_cast<unsigned>((p.H / N + kThreads - 1) / kThreads));
+      hipLaunchKernelGGL(unpermute_vec_kernel<T>, grid, dim3(kThreads), 0, s, hdr, inv, a, probs, o1,
+                         p.H, p.topk);
+    } else {
+      const dim3 grid(static_cast<unsigned>(p.batch), static_cast<unsigned>((p.H + kCols - 1) / kCols));
+      hipLaunchKernelGGL(unpermute_kernel<T>, grid, dim3(kThreads), 0, s, hdr, inv, a, probs, o1, p.H,
+                         p.topk);
+    }
+  } else if (vec) {
+    hipLaunchKernelGGL(unpermute_grad_vec_kernel<T>, dim3(static_cast<unsigned>(p.batch)),
+                       dim3(kThreads), 0, s, hdr, inv, a, b, probs, o1, o2, p.H, p.topk);
   } else {
     hipLaunchKernelGGL(unpermute_grad_kernel<T>, dim3(static_cast<unsigned>(p.batch)), dim3(kThreads),
                        0, s, hdr, inv, a, b, probs, o1, o2, p.H, p.topk);
@@ -180,11 +297,15 @@ hipError_t launch_unpermute(const UnpermutePlan& p, void* ws, const int64_t* eri
                        s, hdr, w.inv, src, static_cast<uint16_t*>(out), row_halves, is_grad ? 1 : 0);
     return hipGetLastError();
   }
+  // 16-byte chunks when every row and pointer is 16-byte aligned
+  const size_t es = p.dtype == PGG_F32 ? 4 : 2;
+  auto a16 = [](const void* q) { return q == nullptr || reinterpret_cast<uintptr_t>(q) % 16 == 0; };
+  const bool vec = (size_t(p.H) * es) % 16 == 0 && a16(permuted) && a16(grad) && a16(out);
   if (p.dtype == PGG_F32)
-    return launch_typed<TF32>(p, w.inv, permuted, grad, probs, out, probs_grad, is_grad, s, hdr);
+    return launch_typed<TF32>(p, w.inv, permuted, grad, probs, out, probs_grad, is_grad, vec, s, hdr);
   if (p.dtype == PGG_BF16)
-    return launch_typed<TBf16>(p, w.inv, permuted, grad, probs, out, probs_grad, is_grad, s, hdr);
-  return launch_typed<TF16>(p, w.inv, permuted, grad, probs, out, probs_grad, is_grad, s, hdr);
+    return launch_typed<TBf16>(p, w.inv, permuted, grad, probs, out, probs_grad, is_grad, vec, s, hdr);
+  return launch_typed<TF16>(p, w.inv, permuted, grad, probs, out, probs_grad, is_grad, vec, s, hdr);
 }
 
 }  // namespace pgg
