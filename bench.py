@@ -147,7 +147,9 @@ def measure_forward(case, w, eri, gl, steps, log):
         achieved = flops / (k_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                 "frac": achieved / peak}
-    roof.update({"kernel": kname, "avg_launch_us": k_ms * 1e3, "launches_per_step": 1})
+    roof.update({"kernel": kname, "avg_launch_us": k_ms * 1e3, "launches_per_step": 1,
+                 "traffic": measured_traffic(kname, case.name),
+                 "traffic_unit": "bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)"})
     log(f"[bench] {case.name} forward: {ms * 1e3:.1f} us/call, {kname} {k_ms * 1e3:.1f} us "
         f"(back to back), {flops / (ms * 1e-3) / 1e12:.1f} TFLOP/s, {bytes_ / (ms * 1e-3) / 1e9:.0f} GB/s")
     return {"ms_per_call": ms, "tflops": flops / (ms * 1e-3) / 1e12,
@@ -217,8 +219,11 @@ def measure_dw(case, gy, eri, gl, steps, log):
         achieved = flops / (k_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                 "frac": achieved / peak}
-    roof.update({"kernel": "dweight", "avg_launch_us": k_ms * 1e3, "launches_per_step": 1})
-    log(f"[bench] {case.name} weight gradient: {ms * 1e3:.1f} us/call, dweight {k_ms * 1e3:.1f} us "
+    kname = "dweight_stream" if case.M <= 64 * case.G else "dweight_large"
+    roof.update({"kernel": kname, "avg_launch_us": k_ms * 1e3, "launches_per_step": 1,
+                 "traffic": measured_traffic(kname, case.name),
+                 "traffic_unit": "bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)"})
+    log(f"[bench] {case.name} weight gradient: {ms * 1e3:.1f} us/call, {kname} {k_ms * 1e3:.1f} us "
         f"(back to back), {flops / (ms * 1e-3) / 1e12:.1f} TFLOP/s, {bytes_ / (ms * 1e-3) / 1e9:.0f} GB/s")
     return {"ms_per_call": ms, "tflops": flops / (ms * 1e-3) / 1e12,
             "gbs": bytes_ / (ms * 1e-3) / 1e9, "roofline": roof,
