@@ -92,20 +92,24 @@ __global__ __launch_bounds__(kConsumeThreads) void consume_kernel(ConsumeArgs a)
 }
 
 // The whole problem is one chunk: every token's rows are all in the ring, so
-// token b simply adds its topK rows in slot order onto +0.  One workgroup per
-// (token, column block).  Slots are taken kBatch at a time: their row indices
+// token b simply adds its topK rows in slot order onto +0.  One one-wave
+// workgroup per (token, column block), so a small batch still spreads over
+// many compute units.  Slots are taken kBatch at a time: their row indices
 // and then their rows are all requested before the first addition, so a
 // token costs two memory latencies per batch instead of two per slot; the
-// additions still run in slot order.
+// additions still run in slot order.  The error word is read beside the row
+// indices and decides only whether d_x is written: every ring read is bounds
+// checked, so nothing read under a bad index leaves the ring.
 constexpr int kBatch = 8;
+constexpr int kTokenThreads = 64;
 
 template <int VEC>
-__global__ __launch_bounds__(kConsumeThreads) void consume_tokens_kernel(ConsumeArgs a) {
+__global__ __launch_bounds__(kTokenThreads) void consume_tokens_kernel(ConsumeArgs a) {
   typedef float vec_t __attribute__((ext_vector_type(VEC)));
-  if (a.hdr->err != kNoError) return;
+  const uint64_t err = a.hdr->err;
   const int64_t b = blockIdx.x / a.col_blocks;
   const int cb = static_cast<int>(blockIdx.x - b * a.col_blocks);
-  const int64_t k = (static_cast<int64_t>(cb) * kConsumeThreads + threadIdx.x) * VEC;
+  const int64_t k = (static_cast<int64_t>(cb) * kTokenThreads + threadIdx.x) * VEC;
   if (k >= a.K) return;
   const int32_t* __restrict__ slots = a.inv + b * a.topk;
   vec_t acc = vec_t(0.0f);
@@ -123,6 +127,7 @@ __global__ __launch_bounds__(kConsumeThreads) void consume_tokens_kernel(Consume
     for (int q = 0; q < kBatch; ++q)
       if (row[q] >= 0 && row[q] < a.M) acc += v[q];
   }
+  if (err != kNoError) return;
   *reinterpret_cast<vec_t*>(a.dx + b * a.K + k) = acc;
 }
 
@@ -146,11 +151,13 @@ hipError_t launch_consume(const Plan& p, int chunk, const WsView& w, float* grad
                                       (int64_t(kConsumeThreads) * vec));
   if (p.max_chunks == 1) {
     // one chunk holds every row: consume by token (chunk_row0[0] == 0 then)
+    a.col_blocks = static_cast<int32_t>((p.K + int64_t(kTokenThreads) * vec - 1) /
+                                        (int64_t(kTokenThreads) * vec));
     const dim3 grid(static_cast<unsigned>(p.batch * a.col_blocks));
     if (vec4)
-      hipLaunchKernelGGL(consume_tokens_kernel<4>, grid, dim3(kConsumeThreads), 0, s, a);
+      hipLaunchKernelGGL(consume_tokens_kernel<4>, grid, dim3(kTokenThreads), 0, s, a);
     else
-      hipLaunchKernelGGL(consume_tokens_kernel<1>, grid, dim3(kConsumeThreads), 0, s, a);
+      hipLaunchKernelGGL(consume_tokens_kernel<1>, grid, dim3(kTokenThreads), 0, s, a);
     return hipGetLastError();
   }
   const dim3 grid(static_cast<unsigned>(int64_t(p.ring_rows) * a.col_blocks));

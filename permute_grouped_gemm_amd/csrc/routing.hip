@@ -158,7 +158,10 @@ __global__ __launch_bounds__(64) void route_place_kernel(const WsHeader* hdr, co
 }
 
 // expanded_x[i] = x[ori[i] / topK]: one workgroup per row, 16-byte pieces when
-// rows are 16-byte aligned.
+// rows are 16-byte aligned, kGatherLoads of them per thread requested before
+// the first is stored.
+constexpr int kGatherLoads = 4;
+
 __global__ __launch_bounds__(256) void route_gather_kernel(const WsHeader* hdr, const int32_t* ori,
                                                            int64_t topk, const char* x, char* ex,
                                                            int64_t row_bytes, int32_t vec) {
@@ -168,8 +171,19 @@ __global__ __launch_bounds__(256) void route_gather_kernel(const WsHeader* hdr, 
   const char* src = x + tok * row_bytes;
   char* dst = ex + i * row_bytes;
   if (vec) {
-    for (int64_t b = threadIdx.x * 16; b < row_bytes; b += 256 * 16)
-      *reinterpret_cast<u32x4_t*>(dst + b) = *reinterpret_cast<const u32x4_t*>(src + b);
+    for (int64_t b0 = threadIdx.x * 16; b0 < row_bytes; b0 += 256 * 16 * kGatherLoads) {
+      u32x4_t v[kGatherLoads];
+#pragma unroll
+      for (int u = 0; u < kGatherLoads; ++u) {
+        const int64_t b = b0 + u * 256 * 16;
+        if (b < row_bytes) v[u] = *reinterpret_cast<const u32x4_t*>(src + b);
+      }
+#pragma unroll
+      for (int u = 0; u < kGatherLoads; ++u) {
+        const int64_t b = b0 + u * 256 * 16;
+        if (b < row_bytes) *reinterpret_cast<u32x4_t*>(dst + b) = v[u];
+      }
+    }
   } else {
     for (int64_t b = threadIdx.x; b < row_bytes; b += 256) dst[b] = src[b];
   }

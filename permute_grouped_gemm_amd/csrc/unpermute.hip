@@ -52,8 +52,7 @@ template <> __device__ __forceinline__ void st<TBf16>(void* p, int64_t i, float 
 template <class T> struct Chunk { static constexpr int N = 16 / int(sizeof(typename T::elem)); };
 
 template <class T>
-__device__ __forceinline__ void ldv(const void* base, int64_t i, float (&v)[Chunk<T>::N]) {
-  const u32x4_t raw = *reinterpret_cast<const u32x4_t*>(static_cast<const typename T::elem*>(base) + i);
+__device__ __forceinline__ void widen(const u32x4_t& raw, float (&v)[Chunk<T>::N]) {
   if constexpr (Chunk<T>::N == 4) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -68,6 +67,19 @@ __device__ __forceinline__ void ldv(const void* base, int64_t i, float (&v)[Chun
       v[2 * k + 1] = ld<T>(&hi, 0);
     }
   }
+}
+
+// Loads that must all be in flight together are issued raw and
+// unconditionally (on an in-bounds address) and only their use is guarded, so
+// that no load waits inside a branch of its own.
+template <class T>
+__device__ __forceinline__ u32x4_t ldraw(const void* base, int64_t i) {
+  return *reinterpret_cast<const u32x4_t*>(static_cast<const typename T::elem*>(base) + i);
+}
+
+template <class T>
+__device__ __forceinline__ void ldv(const void* base, int64_t i, float (&v)[Chunk<T>::N]) {
+  widen<T>(ldraw<T>(base, i), v);
 }
 
 template <class T>
@@ -125,7 +137,11 @@ __global__ __launch_bounds__(kThreads) void unpermute_kernel(const WsHeader* hdr
 }
 
 // The same with 16-byte chunks (rows 16-byte aligned): thread = one chunk of
-// the token's row; grid (batch, chunk blocks of kThreads).
+// the token's row; grid (batch, chunk blocks of kThreads).  Slots are taken
+// kSlotLoads at a time: all their chunks are requested before the first
+// addition, which still runs in slot order.
+constexpr int kSlotLoads = 8;
+
 template <class T>
 __global__ __launch_bounds__(kThreads) void unpermute_vec_kernel(const WsHeader* hdr,
                                                                  const int32_t* inv,
@@ -140,13 +156,24 @@ __global__ __launch_bounds__(kThreads) void unpermute_vec_kernel(const WsHeader*
   float acc[N];
 #pragma unroll
   for (int k = 0; k < N; ++k) acc[k] = 0.0f;
-  for (int64_t j = 0; j < topk; ++j) {
-    const int64_t r = inv[t * topk + j];
-    const float pj = ld<T>(probs, t * topk + j);
-    float v[N];
-    ldv<T>(permuted, r * H + h, v);
+  for (int64_t j0 = 0; j0 < topk; j0 += kSlotLoads) {
+    const int nq = static_cast<int>(topk - j0 < kSlotLoads ? topk - j0 : kSlotLoads);
+    u32x4_t raw[kSlotLoads];
+    float pj[kSlotLoads];
 #pragma unroll
-    for (int k = 0; k < N; ++k) acc[k] += pj * v[k];
+    for (int q = 0; q < kSlotLoads; ++q) {
+      const int64_t j = j0 + (q < nq ? q : 0);   // past the last slot: slot j0 again, unused
+      pj[q] = ld<T>(probs, t * topk + j);
+      raw[q] = ldraw<T>(permuted, static_cast<int64_t>(inv[t * topk + j]) * H + h);
+    }
+#pragma unroll
+    for (int q = 0; q < kSlotLoads; ++q)
+      if (q < nq) {
+        float v[N];
+        widen<T>(raw[q], v);
+#pragma unroll
+        for (int k = 0; k < N; ++k) acc[k] += pj[q] * v[k];
+      }
   }
   stv<T>(out, t * H + h, acc);
 }
@@ -201,7 +228,8 @@ __global__ __launch_bounds__(kThreads) void unpermute_grad_kernel(
   }
 }
 
-// The gradient with 16-byte chunks (rows 16-byte aligned).
+// The gradient with 16-byte chunks for rows too long for the register kernel
+// (rows 16-byte aligned).
 template <class T>
 __global__ __launch_bounds__(kThreads) void unpermute_grad_vec_kernel(
     const WsHeader* hdr, const int32_t* inv, const void* permuted, const void* grad,
@@ -240,6 +268,88 @@ __global__ __launch_bounds__(kThreads) void unpermute_grad_vec_kernel(
   }
 }
 
+// The gradient with the token's grad row held in registers (rows 16-byte
+// aligned, H <= kGradChunks * kThreads chunks): grad[t] is read once, not once
+// per slot.  Each slot's per-thread sum and butterfly run as in the kernel
+// above (same order, so the same bits); the slots' rows and probabilities,
+// kSlotBatch at a time, are staged in LDS, and the waves' sums of those slots
+// wait in LDS for one barrier and are then added in wave order.
+constexpr int kGradChunks = 4;
+constexpr int kSlotBatch = 16;
+
+template <class T>
+__global__ __launch_bounds__(kThreads) void unpermute_grad_reg_kernel(
+    const WsHeader* hdr, const int32_t* inv, const void* permuted, const void* grad,
+    const void* probs, void* perm_grad, void* probs_grad, int64_t H, int64_t topk) {
+  constexpr int N = Chunk<T>::N;
+  __shared__ float s_part[kSlotBatch][kThreads / 64];
+  __shared__ int32_t s_row[kSlotBatch];
+  __shared__ float s_prob[kSlotBatch];
+  if (hdr->err != kNoError) return;
+  const int64_t t = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // this thread's chunks: h = (threadIdx.x + c * kThreads) * N; a chunk past
+  // the row loads chunk 0 instead and is not used
+  int64_t hc[kGradChunks];
+  bool has[kGradChunks];
+  u32x4_t g[kGradChunks];
+#pragma unroll
+  for (int c = 0; c < kGradChunks; ++c) {
+    const int64_t h = static_cast<int64_t>(threadIdx.x + c * kThreads) * N;
+    has[c] = h < H;
+    hc[c] = has[c] ? h : 0;
+    g[c] = ldraw<T>(grad, t * H + hc[c]);
+  }
+  for (int64_t j0 = 0; j0 < topk; j0 += kSlotBatch) {
+    const int nj = static_cast<int>(topk - j0 < kSlotBatch ? topk - j0 : kSlotBatch);
+    // the previous batch's readers of s_row, s_prob and s_part are past the
+    // barrier below it
+    if (static_cast<int>(threadIdx.x) < nj) {
+      s_row[threadIdx.x] = inv[t * topk + j0 + threadIdx.x];
+      s_prob[threadIdx.x] = ld<T>(probs, t * topk + j0 + threadIdx.x);
+    }
+    __syncthreads();
+    for (int q = 0; q < nj; ++q) {
+      const int64_t r = s_row[q];
+      const float pj = s_prob[q];
+      u32x4_t x[kGradChunks];
+#pragma unroll
+      for (int c = 0; c < kGradChunks; ++c) x[c] = ldraw<T>(permuted, r * H + hc[c]);
+      // the dot product adds +0 for an unused chunk (exact: part is never -0),
+      // so every load is consumed outside a branch and none waits inside one
+      float part = 0.0f;
+#pragma unroll
+      for (int c = 0; c < kGradChunks; ++c) {
+        float gv[N], xv[N];
+        widen<T>(g[c], gv);
+        widen<T>(x[c], xv);
+#pragma unroll
+        for (int k = 0; k < N; ++k) part += has[c] ? gv[k] * xv[k] : 0.0f;
+      }
+#pragma unroll
+      for (int c = 0; c < kGradChunks; ++c)
+        if (has[c]) {
+          float gv[N], o[N];
+          widen<T>(g[c], gv);
+#pragma unroll
+          for (int k = 0; k < N; ++k) o[k] = gv[k] * pj;
+          stv<T>(perm_grad, r * H + hc[c], o);
+        }
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) part += __shfl_xor(part, m);
+      if (lane == 0) s_part[q][wave] = part;
+    }
+    __syncthreads();
+    if (static_cast<int>(threadIdx.x) < nj) {
+      float sum = s_part[threadIdx.x][0];
+#pragma unroll
+      for (int w = 1; w < kThreads / 64; ++w) sum += s_part[threadIdx.x][w];
+      st<T>(probs_grad, t * topk + j0 + threadIdx.x, sum);
+    }
+    __syncthreads();
+  }
+}
+
 template <class T>
 hipError_t launch_typed(const UnpermutePlan& p, const int32_t* inv, const void* a, const void* b,
                         const void* probs, void* o1, void* o2, bool grad, bool vec, hipStream_t s,
@@ -256,6 +366,9 @@ hipError_t launch_typed(const UnpermutePlan& p, const int32_t* inv, const void* 
       hipLaunchKernelGGL(unpermute_kernel<T>, grid, dim3(kThreads), 0, s, hdr, inv, a, probs, o1, p.H,
                          p.topk);
     }
+  } else if (vec && p.H <= int64_t(kGradChunks) * kThreads * N) {
+    hipLaunchKernelGGL(unpermute_grad_reg_kernel<T>, dim3(static_cast<unsigned>(p.batch)),
+                       dim3(kThreads), 0, s, hdr, inv, a, b, probs, o1, o2, p.H, p.topk);
   } else if (vec) {
     hipLaunchKernelGGL(unpermute_grad_vec_kernel<T>, dim3(static_cast<unsigned>(p.batch)),
                        dim3(kThreads), 0, s, hdr, inv, a, b, probs, o1, o2, p.H, p.topk);

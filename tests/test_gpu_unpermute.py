@@ -48,7 +48,10 @@ def _bits(a):
     return a.view(np.uint16) if a.dtype.itemsize == 2 else a.view(np.uint32)
 
 
-SHAPES = [(100, 4, 300), (16, 8, 7168), (7, 1, 5), (513, 2, 1031)]
+# (5, 20, 264): more slots than one reduction batch of the register kernel;
+# 4096 and 8200: rows at and past the register kernel's length limit.
+SHAPES = [(100, 4, 300), (16, 8, 7168), (7, 1, 5), (513, 2, 1031), (5, 20, 264), (3, 2, 4096),
+          (3, 2, 8200)]
 
 
 @pytest.mark.parametrize("shape", SHAPES)
