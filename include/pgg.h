@@ -157,7 +157,7 @@ typedef struct {
   int32_t tiles_per_chunk; /* m-tiles whose rows share one ring buffer */
   int32_t max_tiles;       /* upper bound on m-tiles: ceil(M/block_m) + G */
   int32_t max_chunks;      /* chunks enqueued per call */
-  int32_t ring_rows;       /* rows of one ring buffer */
+  int32_t ring_rows;       /* rows of one ring buffer: min(tiles_per_chunk * block_m, M) */
   int32_t fused_prep;      /* 1 when index preparation runs in one workgroup: a kernel of its
                               own, or -- one-chunk weight-streaming plans with G <= 64, when
                               the rows are 16-byte aligned -- a spare workgroup of the

@@ -56,7 +56,7 @@ struct Plan {
   int32_t tc;          // m-tiles per chunk
   int32_t max_tiles;   // ceil(M/bm) + G
   int32_t max_chunks;  // ceil(max_tiles / tc)
-  int32_t ring_rows;   // tc * bm
+  int32_t ring_rows;   // min(tc * bm, M)
   int32_t n_col_tiles; // ceil(K / bn)
   int32_t ksplit;      // forward, few rows per expert: reduction splits (partials in the ring region)
   int32_t kspan;       // reduction elements per split

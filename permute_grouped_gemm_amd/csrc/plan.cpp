@@ -89,7 +89,9 @@ pgg_status make_plan(const pgg_moe_dx_desc* d, Plan* p) {
   if (int64_t(q.bm) * col_blocks_worst >= (int64_t(1) << 23)) return PGG_ERR_UNSUPPORTED;
   q.tc = static_cast<int32_t>(tc);
   q.max_chunks = static_cast<int32_t>((max_tiles + tc - 1) / tc);
-  q.ring_rows = q.tc * q.bm;
+  // a chunk's rows are at most its tiles' capacity and at most M; producers store
+  // only the rows their tiles hold, at (row - first row of the chunk)
+  q.ring_rows = static_cast<int32_t>(std::min<int64_t>(int64_t(q.tc) * q.bm, M));
   q.n_col_tiles = static_cast<int32_t>((K + q.bn - 1) / q.bn);
   q.fused_prep = M <= 16384;
   q.ksplit = 1;

@@ -71,6 +71,18 @@ def test_ring_does_not_grow_with_M():
         assert p["table_bytes"] % 512 == 0
 
 
+def test_ring_never_exceeds_the_intermediate():
+    # the ring holds a chunk's rows at their offset in the chunk: never more than
+    # M rows, so a one-chunk plan needs exactly the [M, K] fp32 rows and no padding
+    for m, g, n, k, topk, dt in ((128, 16, 4096, 7168, 8, BF16), (128, 4, 128, 256, 2, F32),
+                                 (16384, 16, 4096, 7168, 8, BF16), (110592, 60, 2048, 7168, 8, F16)):
+        p = pgg.plan_desc(desc(M=m, N=n, G=g, K=k, batch=m // topk, topk=topk, dy=dt))
+        assert p["ring_rows"] == min(p["tiles_per_chunk"] * p["block_m"], m)
+        assert p["ring_bytes"] == p["ring_rows"] * k * 4 <= m * k * 4
+        if p["max_chunks"] == 1:
+            assert p["ring_rows"] == m
+
+
 def test_plan_regimes():
     assert pgg.plan_desc(desc(dy=F32))["regime"] == 2
     decode = pgg.plan_desc(desc(M=128, N=4096, G=16, K=7168, batch=16, topk=8, dy=BF16))
