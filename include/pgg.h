@@ -334,7 +334,7 @@ pgg_status pgg_moe_dw_kernel_time(const pgg_moe_fwd_desc* desc, const void* x, c
  * the tables unique), so repeated calls give identical tables.  An id outside
  * [0, experts) sets the workspace error word (PGG_DEV_EXPERT_RANGE, read with
  * pgg_moe_dx_read_device_error); the outputs are then unspecified.  Limits:
- * experts <= 8192 and M < 2^31 (PGG_ERR_UNSUPPORTED beyond).  Pointers:
+ * experts <= 8192, M < 2^31 and x_cols < 2^25 (PGG_ERR_UNSUPPORTED beyond).  Pointers:
  * expert_ids and the int64 outputs 8-byte aligned, x / expanded_x aligned to
  * their element size; workspace 256-byte aligned.
  */

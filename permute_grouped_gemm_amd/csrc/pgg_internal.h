@@ -145,7 +145,7 @@ hipError_t launch_unpermute(const UnpermutePlan& p, void* ws, const int64_t* eri
 struct RoutePlan {
   int64_t M, G, topk, K;
   int32_t dtype, nblocks;
-  size_t off_header, off_table, off_bad, off_offsets, off_ori, total;
+  size_t off_header, off_table, off_bad, off_offsets, off_rows, total;
 };
 pgg_status make_routing_plan(const pgg_moe_routing_desc* desc, RoutePlan* plan);
 hipError_t launch_routing(const RoutePlan& p, const int64_t* ids, const void* x, int64_t* group_list,

@@ -159,12 +159,15 @@ pgg_status make_fwd_plan(const pgg_moe_fwd_desc* d, Plan* p) {
   // Few rows per expert: each tile streams its expert's weight columns over
   // the whole reduction.  When the tiles alone would leave the GPU short of
   // workgroups (at most max_tiles x col_tiles have work), the reduction is
-  // split so about 1024 workgroups stream at once; each split writes an fp32
-  // partial of y and a reduction kernel adds them in split order.
+  // split so that up to about 512 workgroups stream at once: one per resident
+  // slot (two per compute unit).  More would run as a second, partly empty
+  // wave (at the decode shape 2 splits took 133 us, 3 took 146 us, 4 took
+  // 139 us).  Each split writes an fp32 partial of y and a reduction kernel
+  // adds them in split order.
   q.ksplit = 1;
   q.kspan = static_cast<int32_t>(K);
   if (q.regime == kStream) {
-    constexpr int64_t kStage = 64, kMinSpan = 512, kTarget = 1024;
+    constexpr int64_t kStage = 64, kMinSpan = 512, kTarget = 512;
     const int64_t units = max_tiles * col_tiles;
     int64_t split = (kTarget + units - 1) / units;
     split = std::min<int64_t>(split, std::max<int64_t>(1, K / kMinSpan));
@@ -202,6 +205,9 @@ pgg_status make_routing_plan(const pgg_moe_routing_desc* d, RoutePlan* p) {
   const int64_t M = d->batch * d->topk;
   constexpr int64_t kBlockPos = 1024;
   if (M >= (int64_t(1) << 31) - 1 || d->experts > 8192) return PGG_ERR_UNSUPPORTED;
+  // the gather splits a row into pieces of at least 4 KiB along a grid
+  // dimension of at most 65535
+  if (d->x_cols >= (int64_t(1) << 25)) return PGG_ERR_UNSUPPORTED;
   const int64_t nblocks = (M + kBlockPos - 1) / kBlockPos;
   if (nblocks * d->experts >= (int64_t(1) << 28)) return PGG_ERR_UNSUPPORTED;
   RoutePlan q{};
@@ -216,7 +222,7 @@ pgg_status make_routing_plan(const pgg_moe_routing_desc* d, RoutePlan* p) {
   q.off_table = off;   off = align_up(off + sizeof(int32_t) * size_t(nblocks * q.G), kRegionAlign);
   q.off_bad = off;     off = align_up(off + sizeof(int64_t) * size_t(nblocks), kRegionAlign);
   q.off_offsets = off; off = align_up(off + sizeof(int64_t) * size_t(q.G + 1), kRegionAlign);
-  q.off_ori = off;     off = align_up(off + sizeof(int32_t) * size_t(M), kRegionAlign);
+  q.off_rows = off;    off = align_up(off + sizeof(int32_t) * size_t(M), kRegionAlign);
   q.total = off;
   *p = q;
   return PGG_OK;

@@ -14,8 +14,10 @@
 // per-block bases and expert offsets, a placement pass in which one wave per
 // block walks its positions in order (a lane's rank among the earlier lanes
 // of the same expert comes from comparing lane by lane, and the last lane of
-// each expert advances that expert's running count), and the optional row
-// gather.  An id outside [0, G) sets the workspace error word (the smallest
+// each expert advances that expert's running count; it also keeps the
+// expanded row of every position in the workspace), and the optional row
+// gather, by token: each token's row is read once and stored to its topK
+// expanded rows.  An id outside [0, G) sets the workspace error word (the smallest
 // offending position wins) and leaves the outputs unspecified.
 #include "pgg_device.h"
 
@@ -122,7 +124,7 @@ __global__ __launch_bounds__(kScanThreads) void route_scan_kernel(WsHeader* hdr,
 // One wave per block: positions in order, 64 at a time.
 __global__ __launch_bounds__(64) void route_place_kernel(const WsHeader* hdr, const int64_t* ids,
                                                          int64_t M, int32_t G, const int32_t* table,
-                                                         const int64_t* offsets, int32_t* ori,
+                                                         const int64_t* offsets, int32_t* row_of,
                                                          int64_t* eri_gather, int64_t* eri_scatter) {
   __shared__ int32_t run[kMaxExperts];
   if (hdr->err != kNoError) return;
@@ -147,7 +149,7 @@ __global__ __launch_bounds__(64) void route_place_kernel(const WsHeader* hdr, co
     int32_t row = 0;
     if (e >= 0) {
       row = run[e] + rank;
-      ori[row] = static_cast<int32_t>(p);
+      row_of[p] = row;
       if (eri_gather) eri_gather[row] = p;
       if (eri_scatter) eri_scatter[p] = row;
     }
@@ -157,35 +159,51 @@ __global__ __launch_bounds__(64) void route_place_kernel(const WsHeader* hdr, co
   }
 }
 
-// expanded_x[i] = x[ori[i] / topK]: one workgroup per row, 16-byte pieces when
-// rows are 16-byte aligned, kGatherLoads of them per thread requested before
-// the first is stored.
+// expanded_x[row_of[b * topK + j]] = x[b] for every slot j: workgroup
+// (b, y) reads piece y of token b's row once, kGatherLoads 16-byte chunks per
+// thread at a time (rows 16-byte aligned; bytes otherwise), and stores them to
+// the token's topK expanded rows.  Large batches take 16 KiB pieces (one per
+// row at the usual widths: reading a token's row once is what saves the
+// traffic); small ones 4 KiB pieces, so a few tokens still spread over many
+// compute units.  The loads are unconditional, on an in-bounds piece (the
+// thread's first of the group stands in past the row end), so that none waits
+// inside a branch of its own; only the stores are guarded.
 constexpr int kGatherLoads = 4;
+constexpr int64_t kGatherGroup = 256 * 16 * kGatherLoads;   // bytes the workgroup loads at a time
+constexpr int64_t kGatherBigBatch = 2048;
 
-__global__ __launch_bounds__(256) void route_gather_kernel(const WsHeader* hdr, const int32_t* ori,
+__global__ __launch_bounds__(256) void route_gather_kernel(const WsHeader* hdr, const int32_t* row_of,
                                                            int64_t topk, const char* x, char* ex,
-                                                           int64_t row_bytes, int32_t vec) {
+                                                           int64_t row_bytes, int64_t piece,
+                                                           int32_t vec) {
   if (hdr->err != kNoError) return;
-  const int64_t i = blockIdx.x;
-  const int64_t tok = static_cast<uint32_t>(ori[i]) / static_cast<uint32_t>(topk);
-  const char* src = x + tok * row_bytes;
-  char* dst = ex + i * row_bytes;
+  const int64_t b = blockIdx.x;
+  const char* src = x + b * row_bytes;
+  const int32_t* rows = row_of + b * topk;
+  const int64_t p0 = static_cast<int64_t>(blockIdx.y) * piece;
+  const int64_t p1 = row_bytes < p0 + piece ? row_bytes : p0 + piece;
   if (vec) {
-    for (int64_t b0 = threadIdx.x * 16; b0 < row_bytes; b0 += 256 * 16 * kGatherLoads) {
+    for (int64_t b0 = p0 + threadIdx.x * 16; b0 < p1; b0 += kGatherGroup) {
       u32x4_t v[kGatherLoads];
 #pragma unroll
       for (int u = 0; u < kGatherLoads; ++u) {
-        const int64_t b = b0 + u * 256 * 16;
-        if (b < row_bytes) v[u] = *reinterpret_cast<const u32x4_t*>(src + b);
+        const int64_t bb = b0 + u * 256 * 16;
+        v[u] = *reinterpret_cast<const u32x4_t*>(src + (bb < p1 ? bb : b0));
       }
+      for (int64_t j = 0; j < topk; ++j) {
+        char* dst = ex + static_cast<int64_t>(rows[j]) * row_bytes;
 #pragma unroll
-      for (int u = 0; u < kGatherLoads; ++u) {
-        const int64_t b = b0 + u * 256 * 16;
-        if (b < row_bytes) *reinterpret_cast<u32x4_t*>(dst + b) = v[u];
+        for (int u = 0; u < kGatherLoads; ++u) {
+          const int64_t bb = b0 + u * 256 * 16;
+          if (bb < p1) *reinterpret_cast<u32x4_t*>(dst + bb) = v[u];
+        }
       }
     }
   } else {
-    for (int64_t b = threadIdx.x; b < row_bytes; b += 256) dst[b] = src[b];
+    for (int64_t c = p0 + threadIdx.x; c < p1; c += 256) {
+      const char v = src[c];
+      for (int64_t j = 0; j < topk; ++j) ex[static_cast<int64_t>(rows[j]) * row_bytes + c] = v;
+    }
   }
 }
 
@@ -199,7 +217,7 @@ hipError_t launch_routing(const RoutePlan& p, const int64_t* ids, const void* x,
   int32_t* table = reinterpret_cast<int32_t*>(b + p.off_table);
   int64_t* bad = reinterpret_cast<int64_t*>(b + p.off_bad);
   int64_t* offsets = reinterpret_cast<int64_t*>(b + p.off_offsets);
-  int32_t* ori = reinterpret_cast<int32_t*>(b + p.off_ori);
+  int32_t* row_of = reinterpret_cast<int32_t*>(b + p.off_rows);
   hipLaunchKernelGGL(route_count_kernel, dim3(p.nblocks), dim3(kCountThreads), 0, s, ids,
                      p.M, static_cast<int32_t>(p.G), table, bad);
   hipError_t e = hipGetLastError();
@@ -208,13 +226,16 @@ hipError_t launch_routing(const RoutePlan& p, const int64_t* ids, const void* x,
                      p.nblocks, static_cast<int32_t>(p.G), offsets, group_list);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(route_place_kernel, dim3(p.nblocks), dim3(64), 0, s, hdr, ids, p.M,
-                     static_cast<int32_t>(p.G), table, offsets, ori, eri_gather, eri_scatter);
+                     static_cast<int32_t>(p.G), table, offsets, row_of, eri_gather, eri_scatter);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (expanded_x && p.K > 0) {
     const int64_t row_bytes = p.K * (p.dtype == PGG_F32 ? 4 : 2);
-    hipLaunchKernelGGL(route_gather_kernel, dim3(static_cast<unsigned>(p.M)), dim3(256), 0, s, hdr,
-                       ori, p.topk, static_cast<const char*>(x), static_cast<char*>(expanded_x),
-                       row_bytes, vec ? 1 : 0);
+    const int64_t batch = p.M / p.topk;
+    const int64_t piece = batch >= kGatherBigBatch ? kGatherGroup : kGatherGroup / 4;
+    const dim3 grid(static_cast<unsigned>(batch), static_cast<unsigned>((row_bytes + piece - 1) / piece));
+    hipLaunchKernelGGL(route_gather_kernel, grid, dim3(256), 0, s, hdr, row_of, p.topk,
+                       static_cast<const char*>(x), static_cast<char*>(expanded_x), row_bytes, piece,
+                       vec ? 1 : 0);
     e = hipGetLastError();
   }
   return e;

@@ -171,6 +171,10 @@ def test_forward_plan_regimes():
     assert plan(dx=F32)["regime"] == 2
     dec = plan(batch=16, topk=8, G=16, K=7168, N=4096, dx=BF16)
     assert dec["regime"] == 1 and dec["block_m"] == 32 and dec["max_chunks"] == 1
+    # decode: at most (128/32 + 16) x 16 = 320 tile-columns have work, so the
+    # reduction is split in 2 (up to 640 workgroups; 384 at the decode routing,
+    # all resident at 2 per compute unit): the ring holds the two fp32 partials
+    assert dec["ring_rows"] == 2 * 128 and dec["ring_bytes"] == 2 * 128 * 4096 * 4
     big = plan(batch=13824, topk=8, G=60, K=7168, N=2048, dx=F16)
     assert big["regime"] == 0 and big["block_m"] == 256 and big["ring_bytes"] == 0
     assert big["max_tiles"] == -(-110592 // 256) + 60 == big["tiles_per_chunk"]
@@ -207,6 +211,8 @@ def test_routing_descriptor_checks():
         d = pgg.make_routing_desc(**bad)
         assert L.pgg_moe_routing_workspace_size(ctypes.byref(d), ctypes.byref(n)) == pgg.ERR_INVALID_ARG
     d = pgg.make_routing_desc(4, 2, 9000)
+    assert L.pgg_moe_routing_workspace_size(ctypes.byref(d), ctypes.byref(n)) == pgg.ERR_UNSUPPORTED
+    d = pgg.make_routing_desc(4, 2, 8, 1 << 25, F32)      # rows too long for the gather's grid
     assert L.pgg_moe_routing_workspace_size(ctypes.byref(d), ctypes.byref(n)) == pgg.ERR_UNSUPPORTED
     d = pgg.make_routing_desc(13824, 8, 60, 7168, F16)
     assert L.pgg_moe_routing_workspace_size(ctypes.byref(d), ctypes.byref(n)) == pgg.OK

@@ -51,7 +51,10 @@ def test_routing_tables_bit_exact(orc, kw):
     np.testing.assert_array_equal(es, o_t1)
 
 
-@pytest.mark.parametrize("dtype,K", [("f32", 96), ("bf16", 7168), ("f16", 13)])
+# rows of one 4 KiB gather piece, several pieces with a short tail (bf16 7168),
+# and rows that are not 16-byte multiples (byte copies), one of them three pieces
+# long; the large batch takes 16 KiB pieces
+@pytest.mark.parametrize("dtype,K", [("f32", 96), ("bf16", 7168), ("f16", 13), ("f16", 4099)])
 def test_routing_expanded_x(orc, dtype, K):
     c = synth.make_case(300, 4, 9, K, 1, dtype, seed=20, empty=(2,))
     x = synth.forward_input(c)
@@ -64,6 +67,18 @@ def test_routing_expanded_x(orc, dtype, K):
     else:
         got = got.numpy()
     np.testing.assert_array_equal(got.view(np.uint8), want.view(np.uint8))
+
+
+@pytest.mark.parametrize("K", [3000, 9000])
+def test_routing_expanded_x_large_batch(orc, K):
+    # 2100 tokens take the 16 KiB pieces: rows of one piece and of two (16384 + 1616 bytes)
+    c = synth.make_case(2100, 2, 8, K, 1, "bf16", seed=24)
+    x = synth.forward_input(c)
+    _, eg, _, ex, ws = _route(c.expert, c.G, x, "bf16")
+    assert pgg.read_device_error(ws) == (pgg.DEV_OK, 0)
+    want = np.ascontiguousarray(x[eg // c.topk])
+    got = ex.cpu().view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(got, want)
 
 
 def test_routing_feeds_the_operators(orc):
