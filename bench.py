@@ -392,7 +392,7 @@ def measure(name, steps, warmup, cpu_baseline, log, forward=True):
                                        which="consume", repeats=steps, out=out, workspace=ws)
     # per-kernel breakdown with an event pair around every launch (each pair
     # adds the launch's dispatch latency; informative only)
-    launches_per_call = 4 + 2 * plan["max_chunks"]
+    launches_per_call = 4 + 2 * plan["max_chunks"] * plan["n_panels"]
     with pgg.KernelTimer(capacity=launches_per_call * steps + 16) as timer:
         for _ in range(steps):
             step()

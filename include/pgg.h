@@ -156,13 +156,18 @@ typedef struct {
   int32_t block_m, block_n;/* output tile: expanded rows x output columns */
   int32_t tiles_per_chunk; /* m-tiles whose rows share one ring buffer */
   int32_t max_tiles;       /* upper bound on m-tiles: ceil(M/block_m) + G */
-  int32_t max_chunks;      /* chunks enqueued per call */
+  int32_t max_chunks;      /* chunks enqueued per panel */
   int32_t ring_rows;       /* rows of one ring buffer: min(tiles_per_chunk * block_m, M) */
   int32_t fused_prep;      /* 1 when index preparation runs in one workgroup: a kernel of its
                               own, or -- one-chunk weight-streaming plans with G <= 64, when
                               the rows are 16-byte aligned -- a spare workgroup of the
                               producer launch; 0: three preparation kernels */
-  size_t ring_bytes;       /* fp32 ring */
+  int32_t n_panels;        /* column panels: the output columns are cut into panels of
+                              panel_cols and each panel runs every chunk (tiled regimes;
+                              the weight-streaming regime keeps one panel) */
+  int32_t reserved0;
+  int64_t panel_cols;      /* columns per panel and fp32 values per ring row */
+  size_t ring_bytes;       /* fp32 ring: ring_rows x panel_cols */
   size_t table_bytes;      /* index / tile tables and header */
   size_t workspace_bytes;  /* total, as returned by pgg_moe_dx_workspace_size */
 } pgg_plan;
@@ -190,7 +195,7 @@ pgg_status pgg_timing_end(pgg_kernel_time* out, int32_t max_out, int32_t* n_out)
 /*
  * Kernel benchmark hook.  Runs one full pgg_moe_dx call (same arguments and
  * contract), which fills the workspace tables, then launches one kernel of
- * the path back to back, `repeats` times per chunk of the call (which = 0:
+ * the path back to back, `repeats` times per (panel, chunk) launch of the call (which = 0:
  * the producer, the grouped-matmul stage; which = 1: the consumer, the
  * routing scatter-add), between two HIP events on `stream`, waits, and
  * returns the average duration of one launch in *avg_ms and the number of

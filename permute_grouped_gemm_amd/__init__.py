@@ -96,12 +96,14 @@ class Plan(ctypes.Structure):
         ("regime", ctypes.c_int32), ("block_m", ctypes.c_int32), ("block_n", ctypes.c_int32),
         ("tiles_per_chunk", ctypes.c_int32), ("max_tiles", ctypes.c_int32),
         ("max_chunks", ctypes.c_int32), ("ring_rows", ctypes.c_int32),
-        ("fused_prep", ctypes.c_int32), ("ring_bytes", ctypes.c_size_t),
+        ("fused_prep", ctypes.c_int32), ("n_panels", ctypes.c_int32),
+        ("reserved0", ctypes.c_int32), ("panel_cols", ctypes.c_int64),
+        ("ring_bytes", ctypes.c_size_t),
         ("table_bytes", ctypes.c_size_t), ("workspace_bytes", ctypes.c_size_t),
     ]
 
     def as_dict(self) -> dict:
-        return {f: getattr(self, f) for f, _ in self._fields_}
+        return {f: getattr(self, f) for f, _ in self._fields_ if f != "reserved0"}
 
 
 class KernelTime(ctypes.Structure):

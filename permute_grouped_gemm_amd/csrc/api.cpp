@@ -6,9 +6,10 @@
 // workspace, and enqueues on the caller's stream:
 //   1. index preparation (one workgroup for small M, three grid-wide passes
 //      otherwise): group offsets, the m-tile table, inv/ori tables, checks;
-//   2. for every chunk of m-tiles: the MFMA producer, which writes the
-//      chunk's fp32 rows into the ring, then the ordered consumer, which adds
-//      them into d_x.
+//   2. for every column panel, and within it every chunk of m-tiles: the
+//      MFMA producer, which writes the chunk's fp32 rows (the panel's
+//      columns) into the ring, then the ordered consumer, which adds them
+//      into those columns of d_x.
 // One-chunk weight-streaming calls with aligned rows and few groups take two
 // launches: the producer runs the preparation in a spare workgroup.  Stream
 // order carries every dependency; there is no host synchronisation and no
@@ -126,20 +127,23 @@ pgg_status enqueue(const Call& c, const void* grad_y, const void* weight,
     }
     if (e == hipSuccess) {
       TimedLaunch t("consume", stream);
-      e = launch_consume(p, 0, w, grad_x, stream);
+      e = launch_consume(p, 0, 0, w, grad_x, stream);
     }
     return e == hipSuccess ? PGG_OK : PGG_ERR_HIP;
   }
   e = enqueue_prep(p, expanded_row_idx, group_list, w, stream);
   const char* pname = produce_kernel_name(p);
-  for (int ch = 0; ch < p.max_chunks && e == hipSuccess; ++ch) {
-    {
-      TimedLaunch t(pname, stream);
-      e = launch_produce(p, ch, grad_y, weight, aligned, w, stream);
+  // column panels one after another; within a panel, chunks in row order
+  for (int pn = 0; pn < p.n_panels && e == hipSuccess; ++pn) {
+    for (int ch = 0; ch < p.max_chunks && e == hipSuccess; ++ch) {
+      {
+        TimedLaunch t(pname, stream);
+        e = launch_produce(p, ch, pn, grad_y, weight, aligned, w, stream);
+      }
+      if (e != hipSuccess) break;
+      TimedLaunch t("consume", stream);
+      e = launch_consume(p, ch, pn, w, grad_x, stream);
     }
-    if (e != hipSuccess) break;
-    TimedLaunch t("consume", stream);
-    e = launch_consume(p, ch, w, grad_x, stream);
   }
   return e == hipSuccess ? PGG_OK : PGG_ERR_HIP;
 }
@@ -210,6 +214,8 @@ void fill_plan(const Plan& p, pgg_plan* out) {
   out->max_tiles = p.max_tiles;
   out->max_chunks = p.max_chunks;
   out->ring_rows = p.ring_rows;
+  out->n_panels = p.n_panels;
+  out->panel_cols = p.panel_cols;
   out->fused_prep = p.fused_prep ? 1 : 0;
   out->ring_bytes = p.ring_bytes;
   out->table_bytes = p.table_bytes;
@@ -268,14 +274,16 @@ pgg_status pgg_moe_dx_kernel_time(const pgg_moe_dx_desc* desc, const void* grad_
     if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) st = PGG_ERR_HIP;
   hipError_t e = st == PGG_OK ? hipEventRecord(ev[0], stream) : hipErrorUnknown;
   for (int32_t r = 0; r < repeats && e == hipSuccess; ++r) {
-    for (int ch = 0; ch < p.max_chunks && e == hipSuccess; ++ch) {
-      if (which == 1)
-        e = launch_consume(p, ch, c.w, grad_x, stream);
-      else if (prepared)
-        e = launch_produce_sweep_prepared(p, grad_y, weight, expanded_row_idx, group_list, c.w,
-                                          stream);
-      else
-        e = launch_produce(p, ch, grad_y, weight, c.aligned, c.w, stream);
+    for (int pn = 0; pn < p.n_panels && e == hipSuccess; ++pn) {
+      for (int ch = 0; ch < p.max_chunks && e == hipSuccess; ++ch) {
+        if (which == 1)
+          e = launch_consume(p, ch, pn, c.w, grad_x, stream);
+        else if (prepared)
+          e = launch_produce_sweep_prepared(p, grad_y, weight, expanded_row_idx, group_list, c.w,
+                                            stream);
+        else
+          e = launch_produce(p, ch, pn, grad_y, weight, c.aligned, c.w, stream);
+      }
     }
   }
   if (e == hipSuccess) e = hipEventRecord(ev[1], stream);
@@ -292,8 +300,9 @@ pgg_status pgg_moe_dx_kernel_time(const pgg_moe_dx_desc* desc, const void* grad_
     st = enqueue(c, grad_y, weight, expanded_row_idx, group_list, grad_x, stream);
     if (st != PGG_OK) return st;
   }
-  *avg_ms = double(ms) / (double(repeats) * double(p.max_chunks));
-  if (launches_per_call) *launches_per_call = p.max_chunks;
+  const int32_t launches = p.max_chunks * p.n_panels;
+  *avg_ms = double(ms) / (double(repeats) * double(launches));
+  if (launches_per_call) *launches_per_call = launches;
   return PGG_OK;
 }
 

@@ -40,8 +40,9 @@ struct GemmArgs {
   const WsHeader* hdr;
   const MTile* tiles;
   const int32_t* chunk_row0;
-  float* ring;              // [ring_rows, K]
+  float* ring;              // [ring_rows, ldc]: columns [k_lo, k_hi) of the panel
   int64_t N, K;
+  int64_t k_lo, k_hi, ldc;
   int32_t chunk, tc, n_col_tiles;
 };
 
@@ -84,8 +85,9 @@ void produce_kernel(GemmArgs a) {
   const MTile tile = a.tiles[tile_idx];
   if (tile.rows <= 0) return;
   const int rows = tile.rows;
-  const int64_t col0 = static_cast<int64_t>(ct) * BN;
-  const int cols = static_cast<int>(min<int64_t>(BN, a.K - col0));
+  const int64_t col0 = a.k_lo + static_cast<int64_t>(ct) * BN;
+  const int cols = static_cast<int>(min<int64_t>(BN, a.k_hi - col0));
+  if (cols <= 0) return;
   const int64_t ring_row0 = static_cast<int64_t>(tile.row0) - a.chunk_row0[a.chunk];
   const int64_t N = a.N;
 
@@ -187,7 +189,7 @@ void produce_kernel(GemmArgs a) {
 
   // Epilogue: accumulator v of lane (lr, lh) is row 8*(v/4) + 4*lh + v%4,
   // column lr of its 32x32 block.
-  float* __restrict__ out = a.ring + ring_row0 * a.K + col0;
+  float* __restrict__ out = a.ring + ring_row0 * a.ldc + (col0 - a.k_lo);
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -196,7 +198,7 @@ void produce_kernel(GemmArgs a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int m = wm * WTM + i * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
-        if (m < rows && n < cols) out[static_cast<int64_t>(m) * a.K + n] = acc[i][j][v];
+        if (m < rows && n < cols) out[static_cast<int64_t>(m) * a.ldc + n] = acc[i][j][v];
       }
     }
   }
@@ -233,10 +235,14 @@ const char* produce_kernel_name(const Plan& p) {
   }
 }
 
-hipError_t launch_produce(const Plan& p, int chunk, const void* grad_y, const void* weight,
-                          bool aligned, const WsView& w, hipStream_t s) {
-  if (p.regime == kStream) return launch_produce_sweep(p, chunk, grad_y, weight, aligned, w, s);
-  if (produce_uses_dma(p, aligned)) return launch_produce_dma(p, chunk, grad_y, weight, w, s);
+hipError_t launch_produce(const Plan& p, int chunk, int panel, const void* grad_y,
+                          const void* weight, bool aligned, const WsView& w, hipStream_t s) {
+  if (p.regime == kStream) {
+    if (panel != 0 || p.n_panels != 1) return hipErrorInvalidValue;
+    return launch_produce_sweep(p, chunk, grad_y, weight, aligned, w, s);
+  }
+  if (produce_uses_dma(p, aligned))
+    return launch_produce_dma(p, chunk, panel, grad_y, weight, w, s);
   GemmArgs args;
   args.A = grad_y;
   args.B = weight;
@@ -246,6 +252,8 @@ hipError_t launch_produce(const Plan& p, int chunk, const void* grad_y, const vo
   args.ring = w.ring;
   args.N = p.N;
   args.K = p.K;
+  panel_range(p, panel, &args.k_lo, &args.k_hi);
+  args.ldc = p.panel_cols;
   args.chunk = chunk;
   args.tc = p.tc;
   args.n_col_tiles = p.n_col_tiles;

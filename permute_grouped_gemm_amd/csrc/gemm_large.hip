@@ -67,8 +67,9 @@ struct LargeArgs {
   const WsHeader* hdr;
   const MTile* tiles;
   const int32_t* chunk_row0;
-  float* ring;
+  float* ring;              // [ring_rows, ldc]: columns [k_lo, k_hi) of the panel
   int64_t N, K;
+  int64_t k_lo, k_hi, ldc;
   int32_t chunk, tc, n_col_tiles;
 };
 
@@ -88,8 +89,9 @@ void produce_large_kernel(LargeArgs a) {
   const MTile tile = a.tiles[tile_idx];
   if (tile.rows <= 0) return;
   const int rows = tile.rows;
-  const int64_t col0 = static_cast<int64_t>(ct) * kBN;
-  const int cols = static_cast<int>(min<int64_t>(kBN, a.K - col0));
+  const int64_t col0 = a.k_lo + static_cast<int64_t>(ct) * kBN;
+  const int cols = static_cast<int>(min<int64_t>(kBN, a.k_hi - col0));
+  if (cols <= 0) return;
   const int64_t N = a.N;
 
   const int tid = threadIdx.x;
@@ -198,7 +200,7 @@ void produce_large_kernel(LargeArgs a) {
   // Epilogue: accumulator v of lane (lr, lh) is row 8*(v/4) + 4*lh + v%4,
   // column lr of its 32x32 block.
   const int64_t ring_row0 = static_cast<int64_t>(tile.row0) - a.chunk_row0[a.chunk];
-  float* __restrict__ out = a.ring + ring_row0 * a.K + col0;
+  float* __restrict__ out = a.ring + ring_row0 * a.ldc + (col0 - a.k_lo);
   const bool full = rows == kBM && cols == kBN;
 #pragma unroll
   for (int i = 0; i < kFM; ++i)
@@ -209,7 +211,7 @@ void produce_large_kernel(LargeArgs a) {
       for (int v = 0; v < 16; ++v) {
         const int m = wm * kWTM + i * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
         if (full || (m < rows && n < cols))
-          __builtin_nontemporal_store(acc[i][j][v], out + static_cast<int64_t>(m) * a.K + n);
+          __builtin_nontemporal_store(acc[i][j][v], out + static_cast<int64_t>(m) * a.ldc + n);
       }
     }
 }
@@ -220,8 +222,8 @@ bool produce_uses_dma(const Plan& p, bool aligned) {
   return aligned && p.regime == kLarge && p.dtype != PGG_F32;
 }
 
-hipError_t launch_produce_dma(const Plan& p, int chunk, const void* grad_y, const void* weight,
-                              const WsView& w, hipStream_t s) {
+hipError_t launch_produce_dma(const Plan& p, int chunk, int panel, const void* grad_y,
+                              const void* weight, const WsView& w, hipStream_t s) {
   LargeArgs a;
   a.A = grad_y;
   a.B = weight;
@@ -231,6 +233,8 @@ hipError_t launch_produce_dma(const Plan& p, int chunk, const void* grad_y, cons
   a.ring = w.ring;
   a.N = p.N;
   a.K = p.K;
+  panel_range(p, panel, &a.k_lo, &a.k_hi);
+  a.ldc = p.panel_cols;
   a.chunk = chunk;
   a.tc = p.tc;
   a.n_col_tiles = p.n_col_tiles;

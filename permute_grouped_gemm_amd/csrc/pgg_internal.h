@@ -57,7 +57,9 @@ struct Plan {
   int32_t max_tiles;   // ceil(M/bm) + G
   int32_t max_chunks;  // ceil(max_tiles / tc)
   int32_t ring_rows;   // min(tc * bm, M)
-  int32_t n_col_tiles; // ceil(K / bn)
+  int32_t n_col_tiles; // column tiles of one panel: ceil(panel_cols / bn)
+  int32_t n_panels;    // column panels: ceil(K / panel_cols)
+  int64_t panel_cols;  // columns per panel (a multiple of bn, or K); the ring row length
   int32_t ksplit;      // forward, few rows per expert: reduction splits (partials in the ring region)
   int32_t kspan;       // reduction elements per split
   bool fused_prep;
@@ -81,7 +83,7 @@ struct WsView {
   int32_t* chunk_row0;  // [max_chunks+1]
   int32_t* inv;         // [M]  original position -> expanded row
   int32_t* ori;         // [M]  expanded row -> original position
-  float* ring;          // [ring_rows, K]
+  float* ring;          // [ring_rows, panel_cols]
 };
 
 inline WsView ws_view(const Plan& p, void* ws) {
@@ -107,7 +109,13 @@ hipError_t launch_prep_groups(const Plan& p, const int64_t* group_list, const Ws
 hipError_t launch_prep_index(const Plan& p, const int64_t* eri, const WsView& w, hipStream_t s);
 hipError_t launch_prep_verify(const Plan& p, const int64_t* eri, const WsView& w, hipStream_t s);
 
-// Producer: chunk c's m-tiles x all column tiles -> ring rows.
+// Columns [lo, hi) of panel `panel`.
+inline void panel_range(const Plan& p, int panel, int64_t* lo, int64_t* hi) {
+  *lo = int64_t(panel) * p.panel_cols;
+  *hi = *lo + p.panel_cols < p.K ? *lo + p.panel_cols : p.K;
+}
+
+// Producer: chunk c's m-tiles x the column tiles of one panel -> ring rows.
 bool produce_uses_dma(const Plan& p, bool aligned);
 hipError_t launch_produce_sweep(const Plan& p, int chunk, const void* grad_y, const void* weight,
                                 bool aligned, const WsView& w, hipStream_t s);
@@ -119,13 +127,16 @@ bool sweep_can_prepare(const Plan& p, bool aligned);
 hipError_t launch_produce_sweep_prepared(const Plan& p, const void* grad_y, const void* weight,
                                          const int64_t* eri, const int64_t* gl, const WsView& w,
                                          hipStream_t s);
-hipError_t launch_produce_dma(const Plan& p, int chunk, const void* grad_y, const void* weight,
-                              const WsView& w, hipStream_t s);
-hipError_t launch_produce(const Plan& p, int chunk, const void* grad_y, const void* weight,
-                          bool aligned, const WsView& w, hipStream_t s);
+hipError_t launch_produce_dma(const Plan& p, int chunk, int panel, const void* grad_y,
+                              const void* weight, const WsView& w, hipStream_t s);
+hipError_t launch_produce(const Plan& p, int chunk, int panel, const void* grad_y,
+                          const void* weight, bool aligned, const WsView& w, hipStream_t s);
 
-// Consumer: ordered scatter-add of chunk c's ring rows into d_x.
-hipError_t launch_consume(const Plan& p, int chunk, const WsView& w, float* grad_x,
+// Consumer: ordered scatter-add of chunk c's ring rows (one panel's columns)
+// into d_x.  One chunk and up to kFewChunks chunks per panel are consumed by
+// token; more chunks by ring row.
+constexpr int kFewChunks = 4;
+hipError_t launch_consume(const Plan& p, int chunk, int panel, const WsView& w, float* grad_x,
                           hipStream_t s);
 
 const char* produce_kernel_name(const Plan& p);

@@ -7,6 +7,7 @@
 #include <stdlib.h>
 
 #include <algorithm>
+#include <cmath>
 
 #include "pgg_internal.h"
 
@@ -21,13 +22,79 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 size_t ring_budget() {
   const char* e = getenv("PGG_RING_MB");
   if (e) {
+    // at most 1 GiB: ring offsets stay far below 2^31 bytes
     long mb = strtol(e, nullptr, 10);
-    if (mb > 0) return static_cast<size_t>(mb) << 20;
+    if (mb > 0) return static_cast<size_t>(std::min<long>(mb, 1024)) << 20;
   }
   return size_t(256) << 20;
 }
 
 struct TileShape { int bm, bn; };
+
+// Columns per panel when K is cut into n panels: whole tiles of bn columns.
+int64_t panel_width(int64_t K, int n, int bn) {
+  const int64_t w = (K + n - 1) / n;
+  return std::min<int64_t>(K, (w + bn - 1) / bn * bn);
+}
+
+// m-tiles per chunk when a ring row holds `cols` fp32 columns.
+int64_t tiles_per_chunk(int bm, int64_t cols, size_t budget, int64_t max_tiles) {
+  const size_t per_tile = size_t(bm) * size_t(cols) * sizeof(float);
+  const int64_t tc = static_cast<int64_t>(budget / per_tile);
+  return std::max<int64_t>(1, std::min<int64_t>(tc, max_tiles));
+}
+
+// Panel count.  PGG_PANEL_COLS fixes the panel width (tuning; a fixed
+// setting gives fixed results).  Otherwise a time estimate picks it, with
+// rates measured on MI355X at the large fp16, large fp32 and mid bf16 shapes:
+//  - the consumer reads every ring row once.  With C chunks per panel, each
+//    of a token's topK rows in any chunk alike, the token's rows fall in
+//    E = C (1 - (1 - 1/C)^topK) distinct chunks and its d_x row is read and
+//    written 2E - 1 times (once when C = 1); it moves these bytes at about
+//    6.7 TB/s when consuming by token (at most kFewChunks chunks) and at
+//    about 5 TB/s by ring row (more chunks);
+//  - every panel past the first reads d_y again: about 15 TB/s of extra
+//    reads for the 16-bit producers, which hide most of it behind the
+//    multiply, and 4.7 TB/s for the fp32 producer.
+// The weight-streaming producer keeps one panel.
+int choose_panels(const Plan& q, size_t budget, int64_t max_tiles) {
+  const int64_t max_panels = (q.K + q.bn - 1) / q.bn;
+  if (const char* e = getenv("PGG_PANEL_COLS")) {
+    const long c = strtol(e, nullptr, 10);
+    if (c > 0) {
+      const int64_t w = std::min<int64_t>(q.K, (c + q.bn - 1) / q.bn * q.bn);
+      return static_cast<int>((q.K + w - 1) / w);
+    }
+  }
+  if (q.regime == kStream) return 1;
+  constexpr double kConsumeRate = 6.7, kRowConsumeRate = 5.0;
+  const double reread_rate = q.dtype == PGG_F32 ? 4.7 : 15.0;
+  const double elem = q.dtype == PGG_F32 ? 4.0 : 2.0;
+  const double dy_bytes = double(q.M) * double(q.N) * elem;
+  const double ring_bytes = double(q.M) * double(q.K) * 4.0;
+  const double dx_bytes = double(q.batch) * double(q.K) * 4.0;
+  int best = 1;
+  double best_time = 0.0;
+  int64_t last_width = -1;
+  for (int64_t n = 1; n <= std::min<int64_t>(max_panels, 64); ++n) {
+    const int64_t w = panel_width(q.K, static_cast<int>(n), q.bn);
+    if (w == last_width) continue;   // same width as a smaller count
+    last_width = w;
+    const int64_t panels = (q.K + w - 1) / w;
+    const int64_t tc = tiles_per_chunk(q.bm, w, budget, max_tiles);
+    const int64_t chunks = (max_tiles + tc - 1) / tc;
+    const double c = double(chunks);
+    const double e = c * (1.0 - std::pow(1.0 - 1.0 / c, double(q.topk)));
+    double t = (ring_bytes + dx_bytes * (2.0 * e - 1.0)) /
+               (chunks <= kFewChunks ? kConsumeRate : kRowConsumeRate);
+    t += double(panels - 1) * dy_bytes / reread_rate;
+    if (n == 1 || t < best_time) {
+      best = static_cast<int>(panels);
+      best_time = t;
+    }
+  }
+  return best;
+}
 
 // Output tile per regime: large-M MFMA tiles; for few rows per expert, m-tiles
 // of 32 rows crossed with units of 16 weight rows that a persistent grid
@@ -64,8 +131,10 @@ pgg_status make_plan(const pgg_moe_dx_desc* d, Plan* p) {
     return PGG_ERR_UNSUPPORTED;
 
   Plan q{};
+  q.n_panels = 1;
   q.M = M; q.N = N; q.G = G; q.K = K; q.batch = d->batch; q.topk = d->topk;
   q.row_idx_type = d->row_idx_type;
+  q.panel_cols = q.K;
   q.dtype = d->grad_y_dtype;
   if (q.dtype == PGG_F32) {
     q.regime = kF32;
@@ -80,11 +149,18 @@ pgg_status make_plan(const pgg_moe_dx_desc* d, Plan* p) {
   const int64_t max_tiles = (M + q.bm - 1) / q.bm + G;
   if (max_tiles >= (int64_t(1) << 31)) return PGG_ERR_UNSUPPORTED;
   q.max_tiles = static_cast<int32_t>(max_tiles);
-  const size_t per_tile = size_t(q.bm) * size_t(K) * sizeof(float);
-  int64_t tc = static_cast<int64_t>(ring_budget() / per_tile);
-  tc = std::max<int64_t>(1, std::min<int64_t>(tc, max_tiles));
+  // Column panels: the output columns are cut into panels of panel_cols
+  // (a multiple of the tile width), and every panel runs the whole chunk
+  // sequence over the rows.  A ring row then holds one panel's columns, so a
+  // chunk holds K / panel_cols times more rows: fewer chunks touch each token,
+  // and the consumer re-reads and re-writes fewer d_x rows, at the price of
+  // reading d_y once per panel.
+  const int n_panels = choose_panels(q, ring_budget(), max_tiles);
+  q.n_panels = n_panels;
+  q.panel_cols = panel_width(K, n_panels, q.bn);
+  int64_t tc = tiles_per_chunk(q.bm, q.panel_cols, ring_budget(), max_tiles);
   // keep the consumer grid (ring rows x column blocks of 256) well inside 2^31 work-items
-  const int64_t col_blocks_worst = (K + 255) / 256;
+  const int64_t col_blocks_worst = (int64_t(q.panel_cols) + 255) / 256;
   while (tc > 1 && tc * q.bm * col_blocks_worst >= (int64_t(1) << 23)) tc /= 2;
   if (int64_t(q.bm) * col_blocks_worst >= (int64_t(1) << 23)) return PGG_ERR_UNSUPPORTED;
   q.tc = static_cast<int32_t>(tc);
@@ -92,7 +168,8 @@ pgg_status make_plan(const pgg_moe_dx_desc* d, Plan* p) {
   // a chunk's rows are at most its tiles' capacity and at most M; producers store
   // only the rows their tiles hold, at (row - first row of the chunk)
   q.ring_rows = static_cast<int32_t>(std::min<int64_t>(int64_t(q.tc) * q.bm, M));
-  q.n_col_tiles = static_cast<int32_t>((K + q.bn - 1) / q.bn);
+  // column tiles of one panel (the last panel may use fewer)
+  q.n_col_tiles = static_cast<int32_t>((q.panel_cols + q.bn - 1) / q.bn);
   q.fused_prep = M <= 16384;
   q.ksplit = 1;
   q.kspan = static_cast<int32_t>(N);
@@ -106,7 +183,7 @@ pgg_status make_plan(const pgg_moe_dx_desc* d, Plan* p) {
   q.off_ori = off;      off = align_up(off + sizeof(int32_t) * size_t(M), kRegionAlign);
   q.table_bytes = off;
   q.off_ring = off;
-  q.ring_bytes = size_t(q.ring_rows) * size_t(K) * sizeof(float);
+  q.ring_bytes = size_t(q.ring_rows) * size_t(q.panel_cols) * sizeof(float);
   off = align_up(off + q.ring_bytes, kRegionAlign);
   q.total = off;
   *p = q;
@@ -133,8 +210,10 @@ pgg_status make_fwd_plan(const pgg_moe_fwd_desc* d, Plan* p) {
     return PGG_ERR_UNSUPPORTED;
 
   Plan q{};
+  q.n_panels = 1;
   q.M = M; q.N = K; q.G = G; q.K = N; q.batch = d->batch; q.topk = d->topk;
   q.row_idx_type = d->row_idx_type;
+  q.panel_cols = q.K;
   q.dtype = d->x_dtype;
   if (q.dtype == PGG_F32) {
     q.regime = kF32;

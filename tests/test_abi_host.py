@@ -61,10 +61,11 @@ def test_too_large_is_unsupported():
 
 def test_ring_does_not_grow_with_M():
     K, N, G = 7168, 2048, 60
-    plans = [pgg.plan_desc(desc(M=m, N=N, G=G, K=K, batch=m // 8, topk=8, dy=F16))
-             for m in (110592, 221184, 442368)]
-    assert len({p["ring_bytes"] for p in plans}) == 1
-    for p, m in zip(plans, (110592, 221184, 442368)):
+    ms = (110592, 221184, 442368, 1769472)
+    plans = [pgg.plan_desc(desc(M=m, N=N, G=G, K=K, batch=m // 8, topk=8, dy=F16)) for m in ms]
+    # the ring holds at most 256 MiB whatever M is (narrower panels, then more
+    # chunks), while the [M, K] fp32 intermediate grows to 50 GB
+    for p, m in zip(plans, ms):
         assert p["ring_bytes"] <= 256 << 20
         assert p["workspace_bytes"] < m * K * 4 // 8            # far below the [M,K] fp32 intermediate
         assert p["workspace_bytes"] == p["table_bytes"] + p["ring_bytes"]
@@ -78,7 +79,7 @@ def test_ring_never_exceeds_the_intermediate():
                                  (16384, 16, 4096, 7168, 8, BF16), (110592, 60, 2048, 7168, 8, F16)):
         p = pgg.plan_desc(desc(M=m, N=n, G=g, K=k, batch=m // topk, topk=topk, dy=dt))
         assert p["ring_rows"] == min(p["tiles_per_chunk"] * p["block_m"], m)
-        assert p["ring_bytes"] == p["ring_rows"] * k * 4 <= m * k * 4
+        assert p["ring_bytes"] == p["ring_rows"] * p["panel_cols"] * 4 <= m * k * 4
         if p["max_chunks"] == 1:
             assert p["ring_rows"] == m
 
@@ -91,6 +92,32 @@ def test_plan_regimes():
     assert large["regime"] == 0
     assert large["max_tiles"] == -(-110592 // large["block_m"]) + 60
     assert large["max_chunks"] * large["tiles_per_chunk"] >= large["max_tiles"]
+
+
+def test_column_panels():
+    # panels are whole tiles wide and cover K; the weight-streaming regime keeps one panel
+    for m, g, n, k, topk, dt in ((128, 16, 4096, 7168, 8, BF16), (16384, 16, 4096, 7168, 8, BF16),
+                                 (110592, 60, 2048, 7168, 8, F16), (110592, 60, 2040, 7160, 8, F32),
+                                 (2400, 5, 300, 600, 4, F16)):
+        p = pgg.plan_desc(desc(M=m, N=n, G=g, K=k, batch=m // topk, topk=topk, dy=dt))
+        w = p["panel_cols"]
+        assert p["n_panels"] == -(-k // w) and 0 < w <= k
+        assert w == k or w % p["block_n"] == 0
+        if p["regime"] == 1:
+            assert p["n_panels"] == 1 and w == k
+    # at the large fp16 shape a 256 MiB ring holds 14 chunks of full rows; panels cut
+    # that to at most a few chunks per panel
+    large = pgg.plan_desc(desc(M=110592, N=2048, G=60, K=7168, batch=13824, topk=8, dy=F16))
+    assert large["n_panels"] > 1 and large["max_chunks"] <= 4
+
+
+def test_panel_width_override(monkeypatch):
+    monkeypatch.setenv("PGG_PANEL_COLS", "300")   # rounded up to whole 256-column tiles
+    p = pgg.plan_desc(desc(M=110592, N=2048, G=60, K=7168, batch=13824, topk=8, dy=F16))
+    assert p["panel_cols"] == 512 and p["n_panels"] == 14
+    monkeypatch.setenv("PGG_PANEL_COLS", "100000")   # wider than K: one panel
+    p = pgg.plan_desc(desc(M=110592, N=2048, G=60, K=7168, batch=13824, topk=8, dy=F16))
+    assert p["panel_cols"] == 7168 and p["n_panels"] == 1
 
 
 def test_execute_rejects_before_any_launch():

@@ -84,6 +84,7 @@ def test_integer_inputs_bit_exact(orc, kw, dtype):
 def test_many_chunks_bit_exact(orc, monkeypatch):
     # a 1 MiB ring forces dozens of chunks: chunk-major order must still be exact
     monkeypatch.setenv("PGG_RING_MB", "1")
+    monkeypatch.setenv("PGG_PANEL_COLS", "100000")   # one panel
     case = synth.make_case(300, 4, 6, 1024, 256, "bf16", seed=201, integer=True)
     gy, w, eri, gl = upload(case)
     plan = pgg.plan(gy, w, eri, gl, case.batch, case.topk, 0)
@@ -109,6 +110,45 @@ def test_many_chunks_float(orc, monkeypatch):
     monkeypatch.setenv("PGG_RING_MB", "2")
     case = synth.make_case(900, 4, 12, 768, 512, "f16", seed=202, w_std=0.02, name="chunked")
     _parity(orc, case)
+
+
+# column panels x chunks: every panel runs the whole chunk sequence over its
+# columns; ragged last panels (K tails) and both tiled producers
+PANEL_CASES = [
+    # (ring MiB, panel columns, case arguments)
+    (1, 256, dict(batch=300, topk=4, G=6, K=1000, N=256, dtype="bf16")),    # 4 panels, last 232 wide
+    (1, 512, dict(batch=300, topk=4, G=6, K=1000, N=256, dtype="f16")),     # 2 panels x chunks
+    (1, 128, dict(batch=200, topk=4, G=5, K=600, N=264, dtype="f32")),      # fp32 tiles, one chunk per
+                                                                             # panel, last panel 88 wide
+    (1, 256, dict(batch=100, topk=3, G=4, K=700, N=286, dtype="bf16")),     # unaligned rows
+    (4, 1024, dict(batch=600, topk=8, G=9, K=2000, N=512, dtype="bf16")),   # 7 chunks x 2 panels
+    (32, 1024, dict(batch=600, topk=8, G=9, K=2000, N=512, dtype="bf16")),  # one chunk per panel
+]
+
+
+@pytest.mark.parametrize("ring_mb,cols,kw", PANEL_CASES)
+def test_panels_bit_exact(orc, monkeypatch, ring_mb, cols, kw):
+    monkeypatch.setenv("PGG_RING_MB", str(ring_mb))
+    monkeypatch.setenv("PGG_PANEL_COLS", str(cols))
+    case = synth.make_case(seed=204, integer=True, **kw)
+    gy, w, eri, gl = upload(case)
+    plan = pgg.plan(gy, w, eri, gl, case.batch, case.topk, 0)
+    assert plan["n_panels"] == -(-case.K // plan["panel_cols"]) >= 2, plan
+    got = run(case, tensors=(gy, w, eri, gl))
+    np.testing.assert_array_equal(bits(got), bits(orc.case_dx(case, mode=orc.SLOT)))
+
+
+def test_panels_float_and_repeatable(orc, monkeypatch):
+    monkeypatch.setenv("PGG_RING_MB", "2")
+    monkeypatch.setenv("PGG_PANEL_COLS", "256")
+    case = synth.make_case(900, 4, 12, 1000, 512, "f16", seed=205, w_std=0.02, name="panels")
+    gy, w, eri, gl = upload(case)
+    plan = pgg.plan(gy, w, eri, gl, case.batch, case.topk, 0)
+    assert plan["n_panels"] == 4 and plan["max_chunks"] >= 2, plan
+    first = run(case, tensors=(gy, w, eri, gl))
+    _parity(orc, case, first)
+    for _ in range(3):
+        np.testing.assert_array_equal(bits(run(case, tensors=(gy, w, eri, gl))), bits(first))
 
 
 # ---------------------------------------------------------------- index tables
@@ -303,7 +343,7 @@ def test_kernel_time_hook_keeps_results(orc, which_case, monkeypatch):
     for which in ("produce", "consume"):
         ms, launches = pgg.kernel_time(gy, w, eri, gl, case.batch, case.topk, 0, which=which,
                                        repeats=3, out=out, workspace=ws)
-        assert ms > 0 and launches == plan["max_chunks"], (which, ms, launches)
+        assert ms > 0 and launches == plan["max_chunks"] * plan["n_panels"], (which, ms, launches)
         torch.cuda.synchronize()
         np.testing.assert_array_equal(bits(out.cpu().numpy()), bits(first))
     assert pgg.read_device_error(ws) == (pgg.DEV_OK, 0)
