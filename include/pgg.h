@@ -97,8 +97,9 @@ typedef struct {
 /*
  * Workspace size in bytes for a descriptor (host only; shapes only; no HIP
  * call).  Returns PGG_ERR_INVALID_ARG / PGG_ERR_UNSUPPORTED for descriptors
- * pgg_moe_dx would reject.  The size does not grow with M·K: it holds
- * O(M + G) integer index tables plus a fixed-size fp32 tile ring.
+ * pgg_moe_dx would reject (PGG_ERR_UNSUPPORTED: M >= 2^31, G >= 2^30,
+ * N >= 2^31 or K >= 2^29).  The size does not grow with M·K: it holds
+ * O(M + G) integer index tables plus an fp32 tile ring of at most 256 MiB.
  */
 pgg_status pgg_moe_dx_workspace_size(const pgg_moe_dx_desc* desc, size_t* bytes);
 

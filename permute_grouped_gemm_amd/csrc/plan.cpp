@@ -129,6 +129,8 @@ pgg_status make_plan(const pgg_moe_dx_desc* d, Plan* p) {
   if (M >= (int64_t(1) << 31) - 1) return PGG_ERR_UNSUPPORTED;
   if (G >= (int64_t(1) << 30) || K >= (int64_t(1) << 31) || N >= (int64_t(1) << 31))
     return PGG_ERR_UNSUPPORTED;
+  // the consumer addresses a d_x row (4K bytes) through a 32-bit range
+  if (K >= (int64_t(1) << 29)) return PGG_ERR_UNSUPPORTED;
 
   Plan q{};
   q.n_panels = 1;

@@ -111,6 +111,14 @@ def test_column_panels():
     assert large["n_panels"] > 1 and large["max_chunks"] <= 4
 
 
+def test_wide_rows_unsupported():
+    # a d_x row of 2^29 fp32 columns or more is beyond the consumer's 32-bit ranges
+    st = pgg.lib().pgg_moe_dx_workspace_size(
+        ctypes.byref(desc(M=16, N=16, G=2, K=1 << 29, batch=8, topk=2, dy=BF16)),
+        ctypes.byref(ctypes.c_size_t()))
+    assert st == pgg.ERR_UNSUPPORTED
+
+
 def test_panel_width_override(monkeypatch):
     monkeypatch.setenv("PGG_PANEL_COLS", "300")   # rounded up to whole 256-column tiles
     p = pgg.plan_desc(desc(M=110592, N=2048, G=60, K=7168, batch=13824, topk=8, dy=F16))
