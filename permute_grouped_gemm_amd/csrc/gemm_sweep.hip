@@ -197,6 +197,16 @@ __global__ __launch_bounds__(kSwThreads) void sweep_dma_kernel(SweepArgs a) {
     chunk_base = a.chunk_row0[a.chunk];
   }
   const int nkb = a.nkb;
+  // Every active workgroup takes the same number of units: with
+  // q = ceil(units / grid) units each, only ceil(units / q) workgroups are
+  // needed, and the rest leave, so no half of the grid idles through the
+  // last round while the other half streams.
+  {
+    const int64_t units = static_cast<int64_t>(tiles_here) * nkb;
+    const int64_t per = (units + nwg - 1) / nwg;
+    if (per > 0) nwg = static_cast<int>((units + per - 1) / per);
+  }
+  if (bid >= nwg) return;
   // unit u = t * nkb + kb; this workgroup takes u = bid + j * nwg
   const int t0 = bid / nkb;
   if (t0 >= tiles_here) return;
