@@ -100,6 +100,10 @@ typedef struct {
  * pgg_moe_dx would reject (PGG_ERR_UNSUPPORTED: M >= 2^31, G >= 2^30,
  * N >= 2^31 or K >= 2^29).  The size does not grow with M·K: it holds
  * O(M + G) integer index tables plus an fp32 tile ring of at most 256 MiB.
+ * Two environment variables, read when a plan is made, tune the schedule
+ * (the size and every call planned under the same setting follow them; a
+ * fixed setting gives fixed results): PGG_RING_MB sets the ring bound in MiB
+ * (at most 1024), PGG_PANEL_COLS the width of the column panels.
  */
 pgg_status pgg_moe_dx_workspace_size(const pgg_moe_dx_desc* desc, size_t* bytes);
 
