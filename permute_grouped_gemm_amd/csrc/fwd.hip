@@ -150,7 +150,10 @@ void fwd_kernel(FwdArgs a) {
       const int q = tid + s * NT;
       const int k = q / kRowChunksB, c = q % kRowChunksB;
       const bool k_ok = k0 + k < R;
-      rb[s] = load_chunk<T, ALIGNED>(Wg + (k_ok ? (k0 + k) * C : 0), k_ok, col0 + c * EPC, C);
+      // the weights: non-temporal for few-row tiles (an expert's one m-tile
+      // streams its strip of W[g] once); larger tiles share W[g] through L2
+      rb[s] = load_chunk<T, ALIGNED, (BM <= 32)>(Wg + (k_ok ? (k0 + k) * C : 0), k_ok,
+                                                 col0 + c * EPC, C);
     }
   };
   auto store_stage = [&](int buf) {

@@ -288,23 +288,29 @@ __global__ __launch_bounds__(kSwThreads) void sweep_dma_kernel(SweepArgs a) {
   // lands in slot i % 32.  The second d_y block is loaded only when the tile
   // has rows there, and first, so a wait that assumes the shorter count only
   // ever over-waits on it.
-  auto load_block = [&](const E* base, int rows, int row0, uint32_t dst, int64_t nc) {
+  // weight slabs are read once per call: non-temporal loads; d_y rows are
+  // read by every unit of their tile
+  auto load_block = [&](const E* base, int rows, int row0, uint32_t dst, int64_t nc, bool nt) {
 #pragma unroll
     for (int l = 0; l < kDmaLoads; ++l) {
       const int r0 = row0 + (4 * l + wave) * kDmaRPI;
       const int r = r0 + sub;
       const int64_t n = (nc + (ci ^ (r & 15))) * EPC;
       const bool ok = r < rows && n < N;
-      dma16(ok ? static_cast<const void*>(base + static_cast<int64_t>(r) * N + n) : zero,
-            dst + static_cast<uint32_t>(r0 * kDmaChunks) * 16u);
+      if (nt)
+        dma16_nt(ok ? static_cast<const void*>(base + static_cast<int64_t>(r) * N + n) : zero,
+                 dst + static_cast<uint32_t>(r0 * kDmaChunks) * 16u);
+      else
+        dma16(ok ? static_cast<const void*>(base + static_cast<int64_t>(r) * N + n) : zero,
+              dst + static_cast<uint32_t>(r0 * kDmaChunks) * 16u);
     }
   };
   auto issue = [&](const Cursor& c, int buf) {
     const uint32_t stage = lds_base + static_cast<uint32_t>(buf * kDmaStageSlots) * 16u;
     const int64_t nc = static_cast<int64_t>(c.st) * kDmaChunks;
-    if (c.x.rows > 16) load_block(c.x.A, c.x.rows, 16, stage + kDmaSlotsW * 16u, nc);
-    load_block(c.x.B, c.x.cols, 0, stage, nc);
-    load_block(c.x.A, c.x.rows, 0, stage + kDmaSlotsW * 16u, nc);
+    if (c.x.rows > 16) load_block(c.x.A, c.x.rows, 16, stage + kDmaSlotsW * 16u, nc, false);
+    load_block(c.x.B, c.x.cols, 0, stage, nc, true);
+    load_block(c.x.A, c.x.rows, 0, stage + kDmaSlotsW * 16u, nc, false);
   };
 
   f32x4_t acc[kSwMS];

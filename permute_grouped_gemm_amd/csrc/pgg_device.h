@@ -17,15 +17,18 @@ struct TF32 { using elem = float; static constexpr int kPerChunk = 4; };
 
 
 // Load one 16-byte chunk of a row (elements [n, n + kPerChunk)), zero outside
-// the row or past N.
-template <class T, bool ALIGNED>
+// the row or past N.  NT: aligned chunks are loaded with the non-temporal
+// hint (data read once, such as a weight stream).
+template <class T, bool ALIGNED, bool NT = false>
 __device__ __forceinline__ u32x4_t load_chunk(const typename T::elem* __restrict__ row, bool row_ok,
                                               int64_t n, int64_t N) {
   using E = typename T::elem;
   constexpr int EPC = T::kPerChunk;
   u32x4_t v = {0u, 0u, 0u, 0u};
   if (!row_ok || n >= N) return v;
-  if constexpr (ALIGNED) {
+  if constexpr (ALIGNED && NT) {
+    v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(row + n));
+  } else if constexpr (ALIGNED) {
     v = *reinterpret_cast<const u32x4_t*>(row + n);
   } else {
     E e[EPC];
@@ -106,6 +109,13 @@ __device__ const u32x4_t kZero16 = {0u, 0u, 0u, 0u};
 // register).
 __device__ __forceinline__ void dma16(const void* src, uint32_t m0) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(m0), "v"(src) : "memory", "m0");
+}
+
+// The same load with the non-temporal hint: for data read exactly once (a
+// weight stream), so its lines do not displace operands that are reused.
+__device__ __forceinline__ void dma16_nt(const void* src, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off nt"
                :: "s"(m0), "v"(src) : "memory", "m0");
 }
 
