@@ -51,18 +51,20 @@ struct ConsumeArgs {
 // keep their order.  Tokens with no row in the chunk leave at once.
 constexpr uint32_t kOutside = 0x80000000u;   // byte offset past every buffer here
 
-template <int VEC>
+// AUX: the load's cache policy (2: non-temporal, for ring rows, each read
+// once).
+template <int VEC, int AUX = 0>
 __device__ __forceinline__ void buffer_load(__amdgpu_buffer_rsrc_t r, uint32_t off, float (&v)[VEC]) {
   if constexpr (VEC == 4) {
     typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-    const u32x4 x = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+    const u32x4 x = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX));
     const unsigned x0 = x[0], x1 = x[1], x2 = x[2], x3 = x[3];   // scalar copies (no element bit-casts)
     v[0] = __builtin_bit_cast(float, x0);
     v[1] = __builtin_bit_cast(float, x1);
     v[2] = __builtin_bit_cast(float, x2);
     v[3] = __builtin_bit_cast(float, x3);
   } else {
-    v[0] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+    v[0] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, AUX));
   }
 }
 
@@ -102,7 +104,7 @@ __global__ __launch_bounds__(kChunkThreads) void consume_chunk_kernel(ConsumeArg
       const int64_t ij = j0 + q < a.topk ? slots[j0 + q] : -1;
       in[q] = ij >= r0 && ij < r1;
       const uint32_t off = in[q] ? static_cast<uint32_t>(((ij - r0) * a.ldc + kk) * 4) : kOutside;
-      buffer_load<VEC>(ring, off, v[q]);
+      buffer_load<VEC, 2>(ring, off, v[q]);
     }
 #pragma unroll
     for (int q = 0; q < kBatch; ++q)
@@ -203,7 +205,9 @@ __global__ __launch_bounds__(kTokenThreads) void consume_tokens_kernel(ConsumeAr
 #pragma unroll
     for (int q = 0; q < kBatch; ++q) {
       const bool ok = row[q] >= 0 && row[q] < a.M;
-      v[q] = ok ? *reinterpret_cast<const vec_t*>(a.ring + row[q] * a.ldc + (k - a.k_lo))
+      // each ring row is read once: non-temporal
+      v[q] = ok ? __builtin_nontemporal_load(
+                      reinterpret_cast<const vec_t*>(a.ring + row[q] * a.ldc + (k - a.k_lo)))
                 : vec_t(0.0f);
     }
 #pragma unroll

@@ -71,10 +71,12 @@ __device__ __forceinline__ void widen(const u32x4_t& raw, float (&v)[Chunk<T>::N
 
 // Loads that must all be in flight together are issued raw and
 // unconditionally (on an in-bounds address) and only their use is guarded, so
-// that no load waits inside a branch of its own.
+// that no load waits inside a branch of its own.  Every row is read and
+// written once: the 16-byte loads and stores are non-temporal.
 template <class T>
 __device__ __forceinline__ u32x4_t ldraw(const void* base, int64_t i) {
-  return *reinterpret_cast<const u32x4_t*>(static_cast<const typename T::elem*>(base) + i);
+  return __builtin_nontemporal_load(
+      reinterpret_cast<const u32x4_t*>(static_cast<const typename T::elem*>(base) + i));
 }
 
 template <class T>
@@ -97,7 +99,7 @@ __device__ __forceinline__ void stv(void* base, int64_t i, const float (&v)[Chun
       raw[k] = static_cast<uint32_t>(lo) | (static_cast<uint32_t>(hi) << 16);
     }
   }
-  *reinterpret_cast<u32x4_t*>(static_cast<typename T::elem*>(base) + i) = raw;
+  __builtin_nontemporal_store(raw, reinterpret_cast<u32x4_t*>(static_cast<typename T::elem*>(base) + i));
 }
 
 __global__ void unpermute_reset_kernel(WsHeader* hdr) {
