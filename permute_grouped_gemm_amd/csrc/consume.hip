@@ -7,19 +7,21 @@
 // rows of one chunk and the columns of one panel.
 //
 // Order, with no atomics: chunks run one after another on the stream, and
-// within a chunk every token is handled by one workgroup per column block,
-// which adds the token's rows that lie in the chunk in ascending topK slot j
-// — the order the TileLang token-permute-grad kernel uses for its fp32
-// gather-reduce — onto either +0 (the token's first chunk) or the d_x row
-// left by earlier chunks.  So each element's additions happen in an order
-// fixed by the inputs and the tile schedule alone, and repeated calls are
-// bit-identical.  When the whole problem is one chunk the order is exactly
-// j = 0..topK-1.
+// within a chunk every token with rows there is handled by exactly one
+// workgroup per column block, which adds the token's rows that lie in the
+// chunk in ascending topK slot j — the order the TileLang token-permute-grad
+// kernel uses for its fp32 gather-reduce — onto either +0 (the token's first
+// chunk) or the d_x value left by earlier chunks.  So each element's
+// additions happen in an order fixed by the inputs and the tile schedule
+// alone, and repeated calls are bit-identical.  When the whole problem is
+// one chunk the order is exactly j = 0..topK-1.
 //
-// Slots are taken kBatch at a time: their row indices, and then their ring
-// rows and the token's earlier d_x value, are all requested before the first
-// addition, so a token costs two memory latencies per batch instead of two
-// per slot.
+// Three kernels: by token for one chunk per panel (consume_tokens_kernel) and
+// for a few (consume_chunk_kernel), by ring row for many
+// (consume_rows_kernel).  The token-indexed ones take slots kBatch at a
+// time: their row indices, and then their ring rows and the token's earlier
+// d_x value, are all requested before the first addition, so a token costs
+// two memory latencies per batch instead of two per slot.
 #include "pgg_internal.h"
 
 namespace pgg {
@@ -43,12 +45,11 @@ struct ConsumeArgs {
 
 // A few chunks: one workgroup of kChunkThreads per (token, block of
 // kChunkThreads * VEC columns); most tokens have several rows in each chunk.
-// Ring
-// rows and the earlier d_x value are read with range-checked buffer loads: a
-// slot outside the chunk, or the d_x value of a token's first chunk, gets an
-// offset past the buffer's end, which the hardware answers with zeros without
-// touching memory, so every load is issued unconditionally and the additions
-// keep their order.  Tokens with no row in the chunk leave at once.
+// Ring rows and the earlier d_x value are read with range-checked buffer
+// loads: a slot outside the chunk, or the d_x value of a token's first chunk,
+// gets an offset past the buffer's end, which the hardware answers with zeros
+// without touching memory, so every load is issued unconditionally and the
+// additions keep their order.  Tokens with no row in the chunk leave at once.
 constexpr uint32_t kOutside = 0x80000000u;   // byte offset past every buffer here
 
 // AUX: the load's cache policy (2: non-temporal, for ring rows, each read
