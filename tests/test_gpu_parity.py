@@ -282,19 +282,35 @@ def _sampled(orc, case, got, n=48, seed=0):
         (colsum, s)
 
 
+def _ten_runs(case, first, tensors):
+    # the plan these shapes get by default (column panels, chunk consumers)
+    # must repeat bit for bit
+    for _ in range(9):
+        np.testing.assert_array_equal(bits(run(case, tensors=tensors)), bits(first))
+
+
 def test_decode_bf16_full(orc):
     case = synth.make_config("decode_bf16")
-    _parity(orc, case)
+    tensors = upload(case)
+    first = run(case, tensors=tensors)
+    _parity(orc, case, first)
+    _ten_runs(case, first, tensors)
 
 
 def test_mid_bf16_sampled(orc):
     case = synth.make_config("mid_bf16")
-    _sampled(orc, case, run(case))
+    tensors = upload(case)
+    first = run(case, tensors=tensors)
+    _sampled(orc, case, first)
+    _ten_runs(case, first, tensors)
 
 
 def test_large_f16_sampled(orc):
     case = synth.make_config("large_f16")
-    _sampled(orc, case, run(case))
+    tensors = upload(case)
+    first = run(case, tensors=tensors)
+    _sampled(orc, case, first)
+    _ten_runs(case, first, tensors)
 
 
 @pytest.mark.parametrize("name", ["large_f32", "large_f32_tail"])
