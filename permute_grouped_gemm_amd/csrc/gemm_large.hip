@@ -29,7 +29,9 @@
 //
 // Masked-off lanes (rows past the tile's rows, columns past K, reduction past
 // N) load 16 zero bytes from a constant in global memory instead.  Ring stores are
-// non-temporal: the consumer reads them back from memory, not from this L2.
+// ordinary (temporal) stores: the consumer, which reads each ring row once
+// with non-temporal loads right after this launch, then finds part of the
+// ring in the last-level cache.
 #include "pgg_device.h"
 
 namespace pgg {
@@ -211,7 +213,7 @@ void produce_large_kernel(LargeArgs a) {
       for (int v = 0; v < 16; ++v) {
         const int m = wm * kWTM + i * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
         if (full || (m < rows && n < cols))
-          __builtin_nontemporal_store(acc[i][j][v], out + static_cast<int64_t>(m) * a.ldc + n);
+          out[static_cast<int64_t>(m) * a.ldc + n] = acc[i][j][v];
       }
     }
 }
