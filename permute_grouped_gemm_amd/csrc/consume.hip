@@ -69,7 +69,10 @@ __device__ __forceinline__ void buffer_load(__amdgpu_buffer_rsrc_t r, uint32_t o
   }
 }
 
-constexpr int kChunkThreads = 256;
+// One wave (256 columns with 16-byte accesses): panels are whole tiles of
+// 256 (or 128) columns wide, so no block is left mostly idle (1024-column
+// blocks left a 256-wide remainder block of a 1280-wide panel).
+constexpr int kChunkThreads = 64;
 
 template <int VEC>
 __global__ __launch_bounds__(kChunkThreads) void consume_chunk_kernel(ConsumeArgs a) {
