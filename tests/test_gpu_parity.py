@@ -123,6 +123,10 @@ PANEL_CASES = [
     (1, 256, dict(batch=100, topk=3, G=4, K=700, N=286, dtype="bf16")),     # unaligned rows
     (4, 1024, dict(batch=600, topk=8, G=9, K=2000, N=512, dtype="bf16")),   # 7 chunks x 2 panels
     (32, 1024, dict(batch=600, topk=8, G=9, K=2000, N=512, dtype="bf16")),  # one chunk per panel
+    # K not a multiple of 4: every consumer takes its 4-byte path
+    (1, 256, dict(batch=300, topk=4, G=6, K=1001, N=256, dtype="bf16")),    # chunk consumer, 4 panels
+    (1, 256, dict(batch=600, topk=8, G=9, K=1001, N=512, dtype="f16")),     # row consumer
+    (1, 128, dict(batch=200, topk=4, G=5, K=601, N=264, dtype="f32")),      # token consumer, 5 panels
 ]
 
 
