@@ -534,7 +534,8 @@ hipError_t launch(const Plan& p, const SweepArgs& a, bool aligned, bool fused, h
 }  // namespace
 
 bool sweep_can_prepare(const Plan& p, bool aligned) {
-  return aligned && p.regime == kStream && p.max_chunks == 1 && p.G <= kSweepPrepMaxGroups;
+  return aligned && p.regime == kStream && p.n_panels == 1 && p.max_chunks == 1 &&
+         p.G <= kSweepPrepMaxGroups;
 }
 
 hipError_t launch_produce_sweep(const Plan& p, int chunk, const void* grad_y, const void* weight,

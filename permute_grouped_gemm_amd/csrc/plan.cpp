@@ -58,6 +58,8 @@ int64_t tiles_per_chunk(int bm, int64_t cols, size_t budget, int64_t max_tiles) 
 //    multiply, and 4.7 TB/s for the fp32 producer.
 // The weight-streaming producer keeps one panel.
 int choose_panels(const Plan& q, size_t budget, int64_t max_tiles) {
+  // the weight sweep stores whole K-column ring rows: one panel, whatever the override
+  if (q.regime == kStream) return 1;
   const int64_t max_panels = (q.K + q.bn - 1) / q.bn;
   if (const char* e = getenv("PGG_PANEL_COLS")) {
     const long c = strtol(e, nullptr, 10);
@@ -66,7 +68,6 @@ int choose_panels(const Plan& q, size_t budget, int64_t max_tiles) {
       return static_cast<int>((q.K + w - 1) / w);
     }
   }
-  if (q.regime == kStream) return 1;
   constexpr double kConsumeRate = 6.7, kRowConsumeRate = 5.0;
   const double reread_rate = q.dtype == PGG_F32 ? 4.7 : 15.0;
   const double elem = q.dtype == PGG_F32 ? 4.0 : 2.0;

@@ -128,6 +128,22 @@ def test_panel_width_override(monkeypatch):
     assert p["panel_cols"] == 7168 and p["n_panels"] == 1
 
 
+def test_panel_override_keeps_weight_streaming_in_one_panel(monkeypatch):
+    # the weight sweep stores ring rows of all K columns, so a panel-width
+    # override must not cut a weight-streaming plan into panels
+    monkeypatch.setenv("PGG_PANEL_COLS", "1024")
+    for m, g, n, k, topk in ((128, 16, 4096, 7168, 8), (1024, 16, 4096, 7168, 8)):
+        p = pgg.plan_desc(desc(M=m, N=n, G=g, K=k, batch=m // topk, topk=topk, dy=BF16))
+        assert p["regime"] == 1
+        assert p["n_panels"] == 1 and p["panel_cols"] == k
+        assert p["ring_bytes"] == min(p["ring_rows"], m) * k * 4
+    dec = pgg.plan_desc(desc(M=128, N=4096, G=16, K=7168, batch=16, topk=8, dy=BF16))
+    assert dec["ring_bytes"] == 128 * 7168 * 4
+    # the override still applies to tiled plans
+    p = pgg.plan_desc(desc(M=110592, N=2048, G=60, K=7168, batch=13824, topk=8, dy=F16))
+    assert p["panel_cols"] == 1024 and p["n_panels"] == 7
+
+
 def test_execute_rejects_before_any_launch():
     L = pgg.lib()
     d = desc()
