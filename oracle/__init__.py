@@ -85,8 +85,9 @@ def lib():
         L.orc_scatter.argtypes = [PP, vp, vp, vp, i32, vp, vp, vp]
         L.orc_dx_tokens.argtypes = [PP, vp, i64, vp, vp, vp, ctypes.c_int]
         L.orc_colsum.argtypes = [PP, vp, i64, vp, vp, ctypes.c_int]
+        L.orc_dx_cols.argtypes = [PP, vp, i64, vp, vp, vp, ctypes.c_int]
         for f in ("orc_check", "orc_offsets", "orc_index", "orc_dex", "orc_scatter", "orc_dx_tokens",
-                  "orc_colsum"):
+                  "orc_colsum", "orc_dx_cols"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -206,6 +207,24 @@ def moe_dx_tokens(grad_y, weight, eri, group_list, batch, topk, row_idx_type, dt
                              dx64.ctypes.data, absdot.ctypes.data, nthreads or default_threads())
     if rc:
         raise OracleError(rc, "tokens")
+    return dx32, dx64, absdot
+
+
+def moe_dx_cols(grad_y, weight, eri, group_list, batch, topk, row_idx_type, dtype, cols, *,
+                nthreads=None):
+    """d_x of every token at the listed output columns: (slot-order float32,
+    exact float64, absdot), each [batch, len(cols)].  Step 1 is evaluated
+    only at those columns, so the cost is M * len(cols) * N multiply-adds."""
+    pr, keep = _problem(grad_y, weight, eri, group_list, batch, topk, row_idx_type, dtype)
+    cols = np.ascontiguousarray(cols, dtype=np.int64)
+    n = cols.shape[0]
+    dx32 = np.empty((batch, n), dtype=np.float32)
+    dx64 = np.empty((batch, n), dtype=np.float64)
+    absdot = np.empty((batch, n), dtype=np.float64)
+    rc = lib().orc_dx_cols(ctypes.byref(pr), cols.ctypes.data, n, dx32.ctypes.data,
+                           dx64.ctypes.data, absdot.ctypes.data, nthreads or default_threads())
+    if rc:
+        raise OracleError(rc, "cols")
     return dx32, dx64, absdot
 
 
@@ -401,6 +420,11 @@ def case_fwd(case, x, **kw):
     """moe_fwd on a ``synth.Case`` and its forward input x [batch, K]."""
     return moe_fwd(x, case.weight, case.eri, case.group_list, case.batch, case.topk,
                    case.row_idx_type, case.dtype, **kw)
+
+
+def case_dx_cols(case, cols, **kw):
+    return moe_dx_cols(case.grad_y, case.weight, case.eri, case.group_list, case.batch, case.topk,
+                       case.row_idx_type, case.dtype, cols, **kw)
 
 
 def case_colsum(case, cols, **kw):

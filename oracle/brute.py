@@ -8,6 +8,9 @@ Test infrastructure; shares nothing with the HIP path.
   reduction indices n of an indicator [batch(i) == b] times d_y[i,n] times
   W[g(i),k,n].  It walks every (b, i) pair with the indicator instead of
   inverting the routing index, and finds g(i) by scanning the counts.
+* ``absdot_literal`` is the same double sum over the magnitudes of the
+  terms, |d_y[i,n]| * |W[g(i),k,n]|: the scale of the a-priori error bound
+  of an fp32 evaluation of the formula.
 * ``forward_literal`` is the forward of the same section:
   expanded_x = Permute(x) and y[i,n] = sum_k expanded_x[i,k] * W[g(i),k,n],
   used for the adjoint identity <d_x, x> = <d_y, y(x)>.
@@ -56,6 +59,26 @@ def dx_literal(dy: np.ndarray, W: np.ndarray, eri: np.ndarray, group_list: np.nd
                 continue
             for k in range(K):
                 out[b, k] += indicator * float(np.dot(dy[i, :], W[g_of[i], k, :]))
+    return out
+
+
+def absdot_literal(dy: np.ndarray, W: np.ndarray, eri: np.ndarray, group_list: np.ndarray,
+                   batch: int, topk: int, row_idx_type: int) -> np.ndarray:
+    """sum_i sum_n 1[batch(i)=b] * |dy[i,n]| * |W[g(i),k,n]|, float64, term by term."""
+    dy = np.asarray(dy, dtype=np.float64)
+    W = np.asarray(W, dtype=np.float64)
+    M, N = dy.shape
+    G, K, _ = W.shape
+    g_of = _group_of_rows(group_list, M)
+    pos = _original_position(eri, row_idx_type)
+    out = np.zeros((batch, K), dtype=np.float64)
+    for b in range(batch):
+        for i in range(M):
+            if pos[i] // topk != b:
+                continue
+            for k in range(K):
+                for n in range(N):
+                    out[b, k] += abs(dy[i, n]) * abs(W[g_of[i], k, n])
     return out
 
 

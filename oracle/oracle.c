@@ -465,3 +465,99 @@ int orc_colsum(const orc_problem* pr, const int64_t* cols, int64_t ncols, double
   free(off); free(th); free(w); free(part);
   return ORC_OK;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Both steps for every token, on a subset of output columns                 */
+/* ------------------------------------------------------------------------ */
+
+/* For every token b and each listed column cols[t]: Step 1 for the token's
+ * expanded rows at that column only (a double dot product over n, ascending,
+ * rounded once to float), then Step 2 in slot order j = 0..topK-1:
+ *   dx32[b,t] = (((+0 + (float)e_0) + (float)e_1) + ...),  e_j the Step 1
+ *               value of row inv[b*topK + j] at column cols[t];
+ *   dx64[b,t] = sum_j e_j in double;  absdot[b,t] = the matching sum of
+ *               |d_y|·|W| over every term.
+ * The same values as orc_dx_tokens at those columns, for all tokens, at a
+ * cost of M * ncols * N multiply-adds. */
+typedef struct {
+  const orc_problem* pr;
+  const int64_t* off;
+  const int64_t* inv;
+  const int64_t* cols;
+  int64_t ncols;
+  float* dx32;
+  double* dx64;
+  double* absdot;
+  int64_t begin, end;
+  int failed;
+} cols_work_t;
+
+static void* cols_worker(void* arg) {
+  cols_work_t* w = (cols_work_t*)arg;
+  const orc_problem* pr = w->pr;
+  const int64_t N = pr->N, K = pr->K, nc = w->ncols;
+  double* dyrow = (double*)malloc(sizeof(double) * (size_t)N);
+  if (!dyrow) { w->failed = 1; return NULL; }
+  for (int64_t b = w->begin; b < w->end; ++b) {
+    for (int64_t t = 0; t < nc; ++t) {
+      w->dx32[b * nc + t] = 0.0f;
+      w->dx64[b * nc + t] = 0.0;
+      w->absdot[b * nc + t] = 0.0;
+    }
+    for (int64_t j = 0; j < pr->topk; ++j) {
+      const int64_t i = w->inv[b * pr->topk + j];
+      const int64_t g = expert_of_row(pr->G, w->off, i);
+      for (int64_t n = 0; n < N; ++n) dyrow[n] = load_elem(pr->dtype, pr->grad_y, i * N + n);
+      for (int64_t t = 0; t < nc; ++t) {
+        const int64_t wbase = (g * K + w->cols[t]) * N;
+        double s = 0.0, a = 0.0;
+        for (int64_t n = 0; n < N; ++n) {
+          const double x = load_elem(pr->dtype, pr->weight, wbase + n);
+          s += dyrow[n] * x;
+          a += fabs(dyrow[n]) * fabs(x);
+        }
+        w->dx32[b * nc + t] = w->dx32[b * nc + t] + (float)s;
+        w->dx64[b * nc + t] += s;
+        w->absdot[b * nc + t] += a;
+      }
+    }
+  }
+  free(dyrow);
+  return NULL;
+}
+
+/* Outputs are [batch, ncols]. */
+int orc_dx_cols(const orc_problem* pr, const int64_t* cols, int64_t ncols, float* dx32,
+                double* dx64, double* absdot, int nthreads) {
+  for (int64_t t = 0; t < ncols; ++t)
+    if (cols[t] < 0 || cols[t] >= pr->K) return ORC_ERR_SHAPE;
+  int64_t* off = (int64_t*)malloc(sizeof(int64_t) * (size_t)(pr->G + 1));
+  int64_t* ori = (int64_t*)malloc(sizeof(int64_t) * (size_t)pr->M);
+  int64_t* inv = (int64_t*)malloc(sizeof(int64_t) * (size_t)pr->M);
+  int rc = ORC_ERR_ALLOC;
+  if (off && ori && inv) rc = prepare(pr, off, ori, inv);
+  if (rc == ORC_OK) {
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > pr->batch) nthreads = (int)pr->batch;
+    pthread_t* th = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));
+    cols_work_t* w = (cols_work_t*)calloc((size_t)nthreads, sizeof(cols_work_t));
+    if (!th || !w) {
+      rc = ORC_ERR_ALLOC;
+    } else {
+      for (int t = 0; t < nthreads; ++t) {
+        w[t].pr = pr; w[t].off = off; w[t].inv = inv; w[t].cols = cols; w[t].ncols = ncols;
+        w[t].dx32 = dx32; w[t].dx64 = dx64; w[t].absdot = absdot;
+        w[t].begin = pr->batch * t / nthreads;
+        w[t].end = pr->batch * (t + 1) / nthreads;
+        pthread_create(&th[t], NULL, cols_worker, &w[t]);
+      }
+      for (int t = 0; t < nthreads; ++t) {
+        pthread_join(th[t], NULL);
+        if (w[t].failed) rc = ORC_ERR_ALLOC;
+      }
+    }
+    free(th); free(w);
+  }
+  free(off); free(ori); free(inv);
+  return rc;
+}

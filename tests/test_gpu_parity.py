@@ -286,6 +286,28 @@ def _sampled(orc, case, got, n=48, seed=0):
         (colsum, s)
 
 
+def _edge_columns(case, n_extra=8, seed=0):
+    """Both sides of every 256-column boundary (the large tiles' edges; panel
+    edges and the fp32 path's 128-column tile edges at multiples of 256 are
+    among them), the first and last column, and a few seeded others."""
+    K = case.K
+    edges = [c for m in range(256, K, 256) for c in (m - 1, m)]
+    rng = np.random.default_rng(seed)
+    extra = rng.choice(K, n_extra, replace=False)
+    return np.array(sorted(set([0, K - 1] + edges + [int(c) for c in extra])), dtype=np.int64)
+
+
+def _all_tokens_at_columns(orc, case, got, exact_bits):
+    # every token, at ~64 columns that cross every tile and panel edge
+    cols = _edge_columns(case)
+    d32, d64, ab = orc.case_dx_cols(case, cols)
+    if exact_bits:
+        np.testing.assert_array_equal(bits(np.ascontiguousarray(got[:, cols])), bits(d32))
+    else:
+        check_close(got[:, cols], d64, ab, case.N, case.topk, case.dtype, case.name + " all tokens")
+    return cols
+
+
 def _ten_runs(case, first, tensors):
     # the plan these shapes get by default (column panels, chunk consumers)
     # must repeat bit for bit
@@ -301,28 +323,31 @@ def test_decode_bf16_full(orc):
     _ten_runs(case, first, tensors)
 
 
-def test_mid_bf16_sampled(orc):
+def test_mid_bf16_all_tokens(orc):
     case = synth.make_config("mid_bf16")
     tensors = upload(case)
     first = run(case, tensors=tensors)
     _sampled(orc, case, first)
+    _all_tokens_at_columns(orc, case, first, exact_bits=False)
     _ten_runs(case, first, tensors)
 
 
-def test_large_f16_sampled(orc):
+def test_large_f16_all_tokens(orc):
     case = synth.make_config("large_f16")
     tensors = upload(case)
     first = run(case, tensors=tensors)
     _sampled(orc, case, first)
+    _all_tokens_at_columns(orc, case, first, exact_bits=False)
     _ten_runs(case, first, tensors)
 
 
 @pytest.mark.parametrize("name", ["large_f32", "large_f32_tail"])
-def test_large_f32_sampled_and_deterministic(orc, name):
+def test_large_f32_all_tokens_and_deterministic(orc, name):
     case = synth.make_config(name)
     tensors = upload(case)
     first = run(case, tensors=tensors)
     _sampled(orc, case, first)
+    _all_tokens_at_columns(orc, case, first, exact_bits=False)
     for _ in range(9):
         np.testing.assert_array_equal(bits(run(case, tensors=tensors)), bits(first))
 
@@ -372,7 +397,8 @@ def test_kernel_time_hook_keeps_results(orc, which_case, monkeypatch):
 
 # ---------------------------------------------------------------- exact regime at the workloads' shapes
 
-@pytest.mark.parametrize("name", ["decode_bf16", "mid_bf16", "large_f16", "large_f32_tail"])
+@pytest.mark.parametrize("name", ["decode_bf16", "mid_bf16", "large_f16", "large_f32",
+                                  "large_f32_tail"])
 def test_integer_inputs_bit_exact_at_workload_shapes(orc, name):
     # integer-valued inputs (|values| <= 2) at the named workloads' full
     # shapes: every partial sum is an integer below 2^24 (4 N topK <= 131072),
@@ -385,8 +411,11 @@ def test_integer_inputs_bit_exact_at_workload_shapes(orc, name):
     if case.M <= 4096:
         np.testing.assert_array_equal(bits(got), bits(orc.case_dx(case, mode=orc.SLOT)))
     else:
+        # every token at ~64 columns across all tile and panel edges, and a
+        # sample of whole token rows
+        _all_tokens_at_columns(orc, case, got, exact_bits=True)
         rng = np.random.default_rng(2)
         toks = np.unique(np.concatenate([[0, case.batch - 1],
-                                         rng.choice(case.batch, 64, replace=False)]))
+                                         rng.choice(case.batch, 16, replace=False)]))
         d32, _, _ = orc.case_dx_tokens(case, toks)
         np.testing.assert_array_equal(bits(got[toks]), bits(d32))

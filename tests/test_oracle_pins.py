@@ -77,6 +77,49 @@ def test_oracle_matches_literal_formula(orc, kw, dtype, row_idx_type):
     assert np.all(np.abs(slot.astype(np.float64) - lit) <= bound + 1e-300)
 
 
+@pytest.mark.parametrize("kw", TINY)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("row_idx_type", [0, 1])
+def test_absdot_matches_literal_sum_of_magnitudes(orc, kw, dtype, row_idx_type):
+    # the scale of every elementwise bound, term by term: sum |d_y| |W| over
+    # the token's rows and the reduction, from all three oracle entries
+    c = synth.make_case(dtype=dtype, row_idx_type=row_idx_type, **kw)
+    lit = brute.absdot_literal(_f64(c, c.grad_y), _f64(c, c.weight), c.eri, c.group_list,
+                               c.batch, c.topk, c.row_idx_type)
+    assert np.all(lit >= 0)
+    _, full = orc.case_dx(c, mode=orc.SLOT, want_abs=True)
+    _, _, tok = orc.case_dx_tokens(c, np.arange(c.batch))
+    cols = np.arange(c.K)[::-1].copy()
+    _, _, col = orc.case_dx_cols(c, cols)
+    for got in (full, tok, col[:, ::-1]):
+        np.testing.assert_allclose(got, lit, rtol=1e-13, atol=1e-300)
+
+
+@pytest.mark.parametrize("kw", TINY)
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("row_idx_type", [0, 1])
+def test_column_subset_matches_literal_formula(orc, kw, dtype, row_idx_type):
+    # every token at a subset of columns (repeats and any order allowed):
+    # exact values against the literal formula; the float32 slot-order values
+    # against the full slot-order evaluation bit for bit
+    c = synth.make_case(dtype=dtype, row_idx_type=row_idx_type, **kw)
+    lit = brute.dx_literal(_f64(c, c.grad_y), _f64(c, c.weight), c.eri, c.group_list,
+                           c.batch, c.topk, c.row_idx_type)
+    cols = np.array([c.K - 1, 0, c.K // 2, c.K - 1])
+    d32, d64, ab = orc.case_dx_cols(c, cols)
+    assert d32.shape == d64.shape == ab.shape == (c.batch, cols.size)
+    np.testing.assert_allclose(d64, lit[:, cols], rtol=1e-13,
+                               atol=1e-13 * max(1.0, np.abs(lit).max()))
+    np.testing.assert_array_equal(d32.view(np.uint32), orc.case_dx(c, mode=orc.SLOT)[:, cols].view(np.uint32))
+
+
+def test_column_subset_rejects_out_of_range_columns(orc):
+    c = synth.make_case(4, 2, 3, 5, 7, "f32", seed=10)
+    for bad in ([-1], [c.K]):
+        with pytest.raises(orc.OracleError):
+            orc.case_dx_cols(c, np.array(bad))
+
+
 # ---------------------------------------------------------------- special cases
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
