@@ -130,6 +130,31 @@ pgg_status pgg_moe_dx(const pgg_moe_dx_desc* desc, const void* grad_y, const voi
                       hipStream_t stream);
 
 /*
+ * Allocation-free variant of pgg_moe_dx, for callers that cannot allocate
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation, arguments and results, without the
+ * workspace argument.  The workspace is a fixed device array of 64 MiB inside
+ * the library, one per GPU, held until the process ends; the ring is planned
+ * to fit it (more chunks than pgg_moe_dx may use, so results equal
+ * pgg_moe_dx's bit for bit when both plans coincide and otherwise within the
+ * same fp32 rounding bounds).  It calls no hipMalloc, hipFree or allocating
+ * routine; the first call on a device looks up that device's array.
+ *
+ * device_error: NULL, or a device pointer to 2 int64 (8-byte aligned) that
+ *   receive, after the call's kernels, the device error of this call as
+ *   [pgg_device_error code, detail] ([0, 0] when there is none).
+ * Errors: those of pgg_moe_dx, and PGG_ERR_WORKSPACE_TOO_SMALL when the
+ * index tables plus the ring rows of one m-tile do not fit the 64 MiB (about
+ * M > 8 million expanded rows, or a very wide K).
+ * Every call on a GPU shares that GPU's array, which keeps the last call's
+ * contents (every call rewrites all it reads): calls that overlap on one GPU
+ * (different streams without ordering) race and give unspecified results.
+ */
+pgg_status pgg_moe_dx_noalloc(const pgg_moe_dx_desc* desc, const void* grad_y, const void* weight,
+                              const int64_t* expanded_row_idx, const int64_t* group_list,
+                              float* grad_x, int64_t* device_error, hipStream_t stream);
+
+/*
  * Read the device error word of the last pgg_moe_dx (or pgg_moe_fwd,
  * pgg_moe_dw, pgg_moe_routing, pgg_moe_unpermute[_grad]) that used `workspace`.
  * Synchronises `stream`.  *code receives a pgg_device_error; *detail its

@@ -38,7 +38,7 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = [
-    "moe_dx", "workspace_size", "plan", "read_device_error", "debug_tables", "debug_tiles",
+    "moe_dx", "moe_dx_noalloc", "workspace_size", "plan", "read_device_error", "debug_tables", "debug_tiles",
     "moe_fwd", "fwd_workspace_size", "fwd_plan", "fwd_kernel_time",
     "moe_dw", "dw_workspace_size", "dw_kernel_time", "moe_routing", "moe_unpermute",
     "moe_unpermute_grad",
@@ -134,6 +134,7 @@ def lib():
         L.pgg_moe_dx_workspace_size.argtypes = [PD, ctypes.POINTER(sz)]
         L.pgg_moe_dx.argtypes = [PD, vp, vp, vp, vp, vp, vp, sz, vp]
         L.pgg_moe_dx_read_device_error.argtypes = [vp, vp, ctypes.POINTER(i32), ctypes.POINTER(i64)]
+        L.pgg_moe_dx_noalloc.argtypes = [PD, vp, vp, vp, vp, vp, vp, vp]
         L.pgg_moe_dx_debug_tables.argtypes = [PD, vp, vp, vp, vp]
         L.pgg_moe_dx_debug_tiles.argtypes = [PD, vp, vp, vp, i32, ctypes.POINTER(i32)]
         L.pgg_moe_dx_plan.argtypes = [PD, ctypes.POINTER(Plan)]
@@ -162,7 +163,8 @@ def lib():
         L.pgg_status_string.restype = ctypes.c_char_p
         L.pgg_device_error_string.argtypes = [i32]
         L.pgg_device_error_string.restype = ctypes.c_char_p
-        for f in ("pgg_moe_dx_workspace_size", "pgg_moe_dx", "pgg_moe_dx_read_device_error",
+        for f in ("pgg_moe_dx_workspace_size", "pgg_moe_dx", "pgg_moe_dx_noalloc",
+                  "pgg_moe_dx_read_device_error",
                   "pgg_moe_dx_debug_tables", "pgg_moe_dx_debug_tiles", "pgg_moe_dx_plan",
                   "pgg_moe_dx_kernel_time", "pgg_moe_fwd_workspace_size", "pgg_moe_fwd",
                   "pgg_moe_fwd_plan", "pgg_moe_fwd_kernel_time", "pgg_moe_dw_workspace_size",
@@ -270,6 +272,30 @@ def moe_dx(grad_y: torch.Tensor, weight: torch.Tensor, expanded_row_idx: torch.T
                           workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                           _stream_handle(stream))
     _check(st, "pgg_moe_dx")
+    return out
+
+
+def moe_dx_noalloc(grad_y: torch.Tensor, weight: torch.Tensor, expanded_row_idx: torch.Tensor,
+                   group_list: torch.Tensor, batch: int, topk: int, row_idx_type: int = 0, *,
+                   out: torch.Tensor, device_error: Optional[torch.Tensor] = None,
+                   stream=None) -> torch.Tensor:
+    """pgg_moe_dx_noalloc: the fused backward into ``out`` (float32 [batch, K])
+    with the library's fixed device scratch as workspace; ``device_error``
+    (optional int64 [2] on the GPU) receives [code, detail] of this call."""
+    d = _desc_from_tensors(grad_y, weight, expanded_row_idx, group_list, batch, topk, row_idx_type)
+    for t in (grad_y, weight, expanded_row_idx, group_list):
+        if not t.is_cuda or not t.is_contiguous():
+            raise PggError(ERR_INVALID_ARG, "inputs must be contiguous GPU tensors")
+    if out.dtype != torch.float32 or not out.is_contiguous() or tuple(out.shape) != (int(batch), int(weight.shape[1])):
+        raise PggError(ERR_INVALID_ARG, "out must be a contiguous float32 [batch, K] tensor")
+    if device_error is not None and (device_error.dtype != torch.int64 or device_error.numel() < 2
+                                     or not device_error.is_cuda):
+        raise PggError(ERR_INVALID_ARG, "device_error must be a GPU int64 tensor of 2 elements")
+    st = lib().pgg_moe_dx_noalloc(ctypes.byref(d), grad_y.data_ptr(), weight.data_ptr(),
+                                  expanded_row_idx.data_ptr(), group_list.data_ptr(), out.data_ptr(),
+                                  None if device_error is None else device_error.data_ptr(),
+                                  _stream_handle(stream))
+    _check(st, "pgg_moe_dx_noalloc")
     return out
 
 

@@ -18,7 +18,7 @@ BUILD_DIR = os.path.join(PKG, "_build")
 SOURCES = ["plan.cpp", "api.cpp", "prep.hip", "gemm.hip", "gemm_large.hip", "gemm_sweep.hip", "consume.hip",
            "fwd.hip", "fwd_large.hip", "dw.hip",
            "dw_large.hip", "routing.hip",
-           "unpermute.hip"]
+           "unpermute.hip", "noalloc.hip"]
 ARCH = os.environ.get("PGG_ARCH", "gfx950")
 
 FLAGS = [

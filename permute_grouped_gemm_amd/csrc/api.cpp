@@ -67,12 +67,19 @@ struct Call {
   bool aligned;
 };
 
+// plan: a plan already made for desc (the allocation-free entry point's), or
+// NULL to make the default one
 pgg_status check_call(const pgg_moe_dx_desc* desc, const void* grad_y, const void* weight,
                       const int64_t* expanded_row_idx, const int64_t* group_list,
-                      const float* grad_x, void* workspace, size_t workspace_bytes, Call* c) {
+                      const float* grad_x, void* workspace, size_t workspace_bytes, Call* c,
+                      const Plan* plan = nullptr) {
   Plan& p = c->plan;
-  const pgg_status st = make_plan(desc, &p);
-  if (st != PGG_OK) return st;
+  if (plan) {
+    p = *plan;
+  } else {
+    const pgg_status st = make_plan(desc, &p);
+    if (st != PGG_OK) return st;
+  }
   if (!grad_y || !weight || !expanded_row_idx || !group_list || !grad_x || !workspace)
     return PGG_ERR_INVALID_ARG;
   if (workspace_bytes < p.total) return PGG_ERR_WORKSPACE_TOO_SMALL;
@@ -252,6 +259,25 @@ pgg_status pgg_moe_dx(const pgg_moe_dx_desc* desc, const void* grad_y, const voi
                                    workspace, workspace_bytes, &c);
   if (st != PGG_OK) return st;
   return enqueue(c, grad_y, weight, expanded_row_idx, group_list, grad_x, stream);
+}
+
+pgg_status pgg_moe_dx_noalloc(const pgg_moe_dx_desc* desc, const void* grad_y, const void* weight,
+                              const int64_t* expanded_row_idx, const int64_t* group_list,
+                              float* grad_x, int64_t* device_error, hipStream_t stream) {
+  Plan plan;
+  pgg_status st = make_plan_within(desc, kNoAllocScratchBytes, &plan);
+  if (st != PGG_OK) return st;
+  if (device_error && !is_aligned(device_error, 8)) return PGG_ERR_MISALIGNED;
+  void* scratch = nullptr;
+  if (!grad_y || !weight || !expanded_row_idx || !group_list || !grad_x) return PGG_ERR_INVALID_ARG;
+  if (noalloc_scratch(stream, &scratch) != hipSuccess) return PGG_ERR_HIP;
+  Call c;
+  st = check_call(desc, grad_y, weight, expanded_row_idx, group_list, grad_x, scratch,
+                  kNoAllocScratchBytes, &c, &plan);
+  if (st != PGG_OK) return st;
+  st = enqueue(c, grad_y, weight, expanded_row_idx, group_list, grad_x, stream);
+  if (st != PGG_OK || !device_error) return st;
+  return launch_export_error(c.w.hdr, device_error, stream) == hipSuccess ? PGG_OK : PGG_ERR_HIP;
 }
 
 pgg_status pgg_moe_dx_kernel_time(const pgg_moe_dx_desc* desc, const void* grad_y,

@@ -70,10 +70,23 @@ struct Plan {
 
 // Fills *plan from a descriptor; returns PGG_OK or the rejection status.
 pgg_status make_plan(const pgg_moe_dx_desc* desc, Plan* plan);
+// The same plan with its ring cut so the whole workspace fits max_total bytes
+// (more chunks); PGG_ERR_WORKSPACE_TOO_SMALL when even one m-tile's ring rows
+// and the tables do not fit.
+pgg_status make_plan_within(const pgg_moe_dx_desc* desc, size_t max_total, Plan* plan);
 // The forward's plan: one chunk holding every m-tile, no ring.
 pgg_status make_fwd_plan(const pgg_moe_fwd_desc* desc, Plan* plan);
 // The weight gradient's plan: the forward's validation and tables, no partials.
 pgg_status make_dw_plan(const pgg_moe_fwd_desc* desc, Plan* plan);
+
+// The allocation-free entry point's workspace: a fixed device array of this
+// size per GPU (noalloc.hip).  noalloc_scratch returns the array's device
+// address on the stream's device (looked up once per device);
+// launch_export_error copies a workspace's error word, decoded into
+// [code, detail], to a caller's device buffer.
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+hipError_t noalloc_scratch(hipStream_t stream, void** ptr);
+hipError_t launch_export_error(const WsHeader* hdr, int64_t* out, hipStream_t s);
 
 // Views of the workspace regions.
 struct WsView {

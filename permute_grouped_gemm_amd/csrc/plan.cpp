@@ -110,7 +110,9 @@ TileShape tile_shape(int32_t regime) {
 
 }  // namespace
 
-pgg_status make_plan(const pgg_moe_dx_desc* d, Plan* p) {
+namespace {
+
+pgg_status plan_with_budget(const pgg_moe_dx_desc* d, size_t budget, Plan* p) {
   if (!d || !p) return PGG_ERR_INVALID_ARG;
   const int64_t M = d->grad_y_rows, N = d->grad_y_cols;
   const int64_t G = d->weight_groups, K = d->weight_rows;
@@ -158,10 +160,10 @@ pgg_status make_plan(const pgg_moe_dx_desc* d, Plan* p) {
   // chunk holds K / panel_cols times more rows: fewer chunks touch each token,
   // and the consumer re-reads and re-writes fewer d_x rows, at the price of
   // reading d_y once per panel.
-  const int n_panels = choose_panels(q, ring_budget(), max_tiles);
+  const int n_panels = choose_panels(q, budget, max_tiles);
   q.n_panels = n_panels;
   q.panel_cols = panel_width(K, n_panels, q.bn);
-  int64_t tc = tiles_per_chunk(q.bm, q.panel_cols, ring_budget(), max_tiles);
+  int64_t tc = tiles_per_chunk(q.bm, q.panel_cols, budget, max_tiles);
   // keep the consumer grid (ring rows x column blocks of 256) well inside 2^31 work-items
   const int64_t col_blocks_worst = (int64_t(q.panel_cols) + 255) / 256;
   while (tc > 1 && tc * q.bm * col_blocks_worst >= (int64_t(1) << 23)) tc /= 2;
@@ -189,6 +191,27 @@ pgg_status make_plan(const pgg_moe_dx_desc* d, Plan* p) {
   q.ring_bytes = size_t(q.ring_rows) * size_t(q.panel_cols) * sizeof(float);
   off = align_up(off + q.ring_bytes, kRegionAlign);
   q.total = off;
+  *p = q;
+  return PGG_OK;
+}
+
+}  // namespace
+
+pgg_status make_plan(const pgg_moe_dx_desc* d, Plan* p) {
+  return plan_with_budget(d, ring_budget(), p);
+}
+
+pgg_status make_plan_within(const pgg_moe_dx_desc* d, size_t max_total, Plan* p) {
+  Plan q;
+  pgg_status st = plan_with_budget(d, ring_budget(), &q);
+  if (st != PGG_OK) return st;
+  // the tables' size with the largest possible chunk table (one chunk per m-tile)
+  const size_t tables = q.table_bytes +
+                        align_up(sizeof(int32_t) * size_t(q.max_tiles + 1), kRegionAlign) + kRegionAlign;
+  if (max_total <= tables) return PGG_ERR_WORKSPACE_TOO_SMALL;
+  st = plan_with_budget(d, std::min(ring_budget(), max_total - tables), &q);
+  if (st != PGG_OK) return st;
+  if (q.total > max_total) return PGG_ERR_WORKSPACE_TOO_SMALL;
   *p = q;
   return PGG_OK;
 }

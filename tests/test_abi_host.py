@@ -144,6 +144,20 @@ def test_panel_override_keeps_weight_streaming_in_one_panel(monkeypatch):
     assert p["panel_cols"] == 1024 and p["n_panels"] == 7
 
 
+def test_noalloc_rejects_problems_beyond_its_scratch_before_any_hip_call():
+    # the allocation-free entry point plans into a fixed 64 MiB scratch; index
+    # tables that alone exceed it are refused on the host (fake pointers are
+    # never dereferenced)
+    fake = 0x100000
+    big = desc(M=16 << 20, N=64, G=4, K=64, batch=8 << 20, topk=2, dy=BF16)
+    assert pgg.workspace_size_desc(big) > 64 << 20
+    st = pgg.lib().pgg_moe_dx_noalloc(ctypes.byref(big), fake, fake, fake, fake, fake, None, None)
+    assert st == pgg.ERR_WORKSPACE_TOO_SMALL
+    bad = desc(topk=3)   # batch * topk != M
+    st = pgg.lib().pgg_moe_dx_noalloc(ctypes.byref(bad), fake, fake, fake, fake, fake, None, None)
+    assert st == pgg.ERR_INVALID_ARG
+
+
 def test_execute_rejects_before_any_launch():
     L = pgg.lib()
     d = desc()
