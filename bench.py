@@ -329,7 +329,7 @@ def measure_unpermute(case, eri, steps, log):
     return res
 
 
-def measure(name, steps, warmup, cpu_baseline, log, forward=True):
+def measure(name, steps, warmup, cpu_baseline, log, forward=True, cold_variant=None):
     import numpy as np
     import torch
 
@@ -406,7 +406,9 @@ def measure(name, steps, warmup, cpu_baseline, log, forward=True):
     # inputs (a read leaves no dirty lines to write back during the call);
     # warm calls timed the same way (an event pair per call) for comparison
     cold = None
-    if plan["regime"] == 1:
+    if cold_variant is None:
+        cold_variant = plan["regime"] == 1
+    if cold_variant:
         scrub = torch.ones(128 << 20, dtype=torch.int32, device=dev)
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(2 * steps)]
@@ -463,6 +465,7 @@ def measure(name, steps, warmup, cpu_baseline, log, forward=True):
         "cold_vs_warm": cold, "smi_sclk_after_timing": sclk,
         "workspace_bytes": plan["workspace_bytes"], "ring_bytes": plan["ring_bytes"],
         "d_expanded_x_fp32_bytes": case.M * case.K * 4,
+        "workspace_vs_MK4": plan["workspace_bytes"] / (case.M * case.K * 4),
         "plan": plan,
         "dtype": case.dtype,
         "config": {"workload": name, "batch": case.batch, "topk": case.topk, "M": case.M,
@@ -518,9 +521,30 @@ def oracle_baseline(case, unit, log):
         val = 2.0 * rows * case.N * case.K / dt / 1e12
     log(f"[bench] oracle sample: {n_tok} tokens, {reps} run(s) of {dt:.2f}s on {threads} threads")
     return {"value": val, "unit": unit, "cores": threads, "kind": "oracle",
-            "seconds": dt * reps,
+            "cpu_model": cpu_model(), "seconds": dt * reps,
             "sample": f"d_x rows of tokens 0..{n_tok - 1} ({rows} expanded rows, all K columns) "
                       f"of the same inputs, computed {reps} time(s)"}
+
+
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+# the other workloads of the headline metric's family, each measured as the
+# headline ones are (parity cases too): tiny fp32, mid bf16 (Zipf routing,
+# scatter index; cold variant), large fp32 and its K/N-tail variant
+EXTRA_WORKLOADS = ("tiny_f32", "mid_bf16", "large_f32", "large_f32_tail")
+EXTRA_KEYS = ("value", "unit", "ms_per_step", "tflops", "gbs", "frac_bf16_peak", "frac_hbm",
+              "roofline", "kernels_ms_per_step", "cold_vs_warm", "workspace_bytes", "ring_bytes",
+              "d_expanded_x_fp32_bytes", "workspace_vs_MK4", "config", "dtype", "plan")
 
 
 def under_profiler():
@@ -614,6 +638,8 @@ def main():
     ap.add_argument("--workload", default="decode_bf16")
     ap.add_argument("--no-large", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the tiny, mid and large fp32 workloads (the \"workloads\" object)")
     ap.add_argument("--no-forward", action="store_true",
                     help="skip the forward, weight-gradient, routing and unpermute measurements")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -675,6 +701,17 @@ def main():
         for k in ("forward", "dweight", "routing", "unpermute"):
             if k in large:
                 line["large"][k] = large[k]
+    if not args.no_extra:
+        extra = {}
+        for name in EXTRA_WORKLOADS:
+            if name == args.workload:
+                continue
+            r = measure(name, max(5, args.steps // 2), args.warmup, not args.no_cpu_baseline, log,
+                        forward=False, cold_variant=(name == "mid_bf16"))
+            extra[name] = {k: r[k] for k in EXTRA_KEYS if k in r}
+            if "cpu_baseline" in r:
+                extra[name]["cpu_baseline"] = r["cpu_baseline"]
+        line["workloads"] = extra
     print(json.dumps(line), flush=True)
     return 0
 
