@@ -4,12 +4,18 @@
 // cube output, §2.6.2) on 256x256 output tiles, written into the chunk's ring
 // rows.
 //
-// One workgroup per tile, mapped by the XCD super-block raster (raster<8,4>):
-// the 32 workgroups an XCD runs together share 8 d_y slabs and 4 weight slabs
-// in its L2.
+// Persistent: one workgroup per compute unit walks the launch's tiles
+// t = blockIdx.x + j * gridDim.x in the XCD super-block raster (raster<8,4>;
+// gridDim.x is a multiple of 8, so all of a workgroup's tiles sit on one XCD,
+// and in round j the 32 workgroups of an XCD share 8 d_y slabs and 4 weight
+// slabs in its L2).  A workgroup first reads its tiles' table entries into LDS.
+// The operand loads then run as one stream of stages across its tiles: the
+// next tile's first two stages load during the current tile's last two, so a
+// tile starts without waiting for loads, and its predecessor's ring stores
+// drain while it multiplies.
 //
-// Operand staging is direct global -> LDS (global_load_lds_dwordx4: lane i's
-// 16 bytes land at M0 + 16 i), two stages of 64 reduction elements (64 KiB
+// Operand staging is direct buffer -> LDS (buffer_load_dwordx4 ... lds: lane
+// i's 16 bytes land at M0 + 16 i), two stages of 64 reduction elements (64 KiB
 // each: 256 d_y rows + 256 weight rows of 128 bytes, whole cache lines).  The
 // loads are issued by inline assembly so the compiler does not serialise them
 // with a blanket wait before every LDS read; the waits on their counter are
@@ -18,20 +24,23 @@
 //
 // Per stage and wave (2 x 4 waves, two per SIMD, 128 x 64 fp32 accumulators
 // each): four chunk pairs of 8 MFMA 32x32x16; the fragments of the next pair
-// are read while the current pair multiplies, across stage boundaries too.
-// The second wave on each SIMD keeps the matrix unit fed while the other
-// issues its loads or waits on LDS.
+// are read while the current pair multiplies, across stage and tile
+// boundaries too.  The second wave on each SIMD keeps the matrix unit fed
+// while the other issues its loads or waits on LDS.
 //
 // LDS rows are 128 bytes (8 chunks).  128-bit LDS reads are served 16 lanes
 // at a time over 64 banks (256 bytes = 2 rows); a fragment read puts 16
 // consecutive rows, same chunk, in those lanes, so chunk c of row r sits at
 // slot c ^ ((r >> 1) & 7): the 8 rows of each parity get 8 different slots.
 //
-// Masked-off lanes (rows past the tile's rows, columns past K, reduction past
-// N) load 16 zero bytes from a constant in global memory instead.  Ring stores are
-// ordinary (temporal) stores: the consumer, which reads each ring row once
+// Operands are loaded through buffer resources that end at the tile's last
+// row, so rows past the tile's rows or past K read zeros; chunks past N get an
+// offset outside every buffer and read zeros too.  Ring stores
+// are ordinary (temporal) stores: the consumer, which reads each ring row once
 // with non-temporal loads right after this launch, then finds part of the
 // ring in the last-level cache.
+#include <algorithm>
+
 #include "pgg_device.h"
 
 namespace pgg {
@@ -58,6 +67,8 @@ constexpr int kLoadsPerStage = kLoadsA + kLoadsB;
 constexpr int kSuperM = 8, kSuperN = 4;                // super-block of tiles per XCD round
 constexpr int kSuper = kSuperM * kSuperN;
 constexpr int kXcds = 8;
+constexpr int kRound = kXcds * kSuper;                 // tiles of one raster round (256)
+constexpr int kMaxTilesPerWg = 64;                     // LDS tile-table entries per workgroup
 static_assert(kLoadsPerStage * kStages <= 63, "vmcnt range");
 static_assert(kPairs % 2 == 0, "a stage must end on the second fragment set");
 static_assert(kRowsPerLoad * kWaves * kLoadsA == kBM && kRowsPerLoad * kWaves * kLoadsB == kBN,
@@ -73,7 +84,28 @@ struct LargeArgs {
   int64_t N, K;
   int64_t k_lo, k_hi, ldc;
   int32_t chunk, tc, n_col_tiles;
+  int32_t span;             // raster positions of the launch (a multiple of kRound)
 };
+
+// A tile's operands as buffer resources: its d_y rows and its weight rows
+// (the tile's output columns), each exactly as long as the tile holds rows,
+// so loads of rows past the tile read zeros from the range check.
+struct Operands {
+  __amdgpu_buffer_rsrc_t a, b;
+};
+
+// A byte offset past every operand buffer (they are below 2^31 bytes).
+constexpr uint32_t kOutside = 0x80000000u;
+
+// Direct buffer -> LDS load of 16 bytes per lane: lane i's bytes (at byte
+// offset voff of the buffer; zeros when voff is past its range) land at LDS
+// byte offset m0 + 16 i.  Issued by inline assembly like dma16.  An LDS load
+// reads M0 one wait state after it is written, hence the s_nop; the whole
+// offset is in the vector offset, which the range check covers.
+__device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(m0), "v"(voff), "s"(r) : "memory", "m0");
+}
 
 __device__ __forceinline__ int slot_of(int r, int c) { return c ^ ((r >> 1) & 7); }
 
@@ -82,21 +114,46 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 void produce_large_kernel(LargeArgs a) {
   using E = typename T::elem;
   __shared__ u32x4_t lds[kStages * kStageSlots];
+  // this workgroup's tiles: {g, row0, rows, column tile}; rows 0 = no tile
+  __shared__ int4 tab[kMaxTilesPerWg];
 
   if (a.hdr->err != kNoError) return;
-  int slot, ct;
-  if (!raster<kSuperM, kSuperN>(blockIdx.x, a.tc, a.n_col_tiles, slot, ct)) return;
-  const int64_t tile_idx = static_cast<int64_t>(a.chunk) * a.tc + slot;
-  if (tile_idx >= a.hdr->n_tiles) return;
-  const MTile tile = a.tiles[tile_idx];
-  if (tile.rows <= 0) return;
-  const int rows = tile.rows;
-  const int64_t col0 = a.k_lo + static_cast<int64_t>(ct) * kBN;
-  const int cols = static_cast<int>(min<int64_t>(kBN, a.k_hi - col0));
-  if (cols <= 0) return;
-  const int64_t N = a.N;
-
   const int tid = threadIdx.x;
+  const int grid = static_cast<int>(gridDim.x);
+  const int n_mine = (a.span - static_cast<int>(blockIdx.x) + grid - 1) / grid;
+  {
+    const int n_tiles = a.hdr->n_tiles;
+    for (int j = tid; j < n_mine; j += kThreads) {
+      int slot, ct;
+      int4 e = make_int4(0, 0, 0, 0);
+      if (raster<kSuperM, kSuperN>(static_cast<int>(blockIdx.x) + j * grid, a.tc, a.n_col_tiles,
+                                   slot, ct)) {
+        const int64_t idx = static_cast<int64_t>(a.chunk) * a.tc + slot;
+        const int64_t col0 = a.k_lo + static_cast<int64_t>(ct) * kBN;
+        if (idx < n_tiles && col0 < a.k_hi) {
+          const MTile m = a.tiles[idx];
+          if (m.rows > 0) e = make_int4(m.g, m.row0, m.rows, ct);
+        }
+      }
+      tab[j] = e;
+    }
+  }
+  __syncthreads();
+  // table entry j, the same in every lane (kept in scalar registers)
+  auto entry = [&](int j) {
+    const int4 e = tab[j];
+    return make_int4(__builtin_amdgcn_readfirstlane(e.x), __builtin_amdgcn_readfirstlane(e.y),
+                     __builtin_amdgcn_readfirstlane(e.z), __builtin_amdgcn_readfirstlane(e.w));
+  };
+  auto next_tile = [&](int j) {   // first entry at or after j with rows
+    while (j < n_mine && entry(j).z <= 0) ++j;
+    return j;
+  };
+  int cur = next_tile(0);
+  if (cur >= n_mine) return;
+  int nxt = next_tile(cur + 1);
+
+  const int64_t N = a.N;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave % kWM, wn = wave / kWM;
@@ -106,35 +163,47 @@ void produce_large_kernel(LargeArgs a) {
   // holds chunk (lane%8) ^ ((r0/2)%8) -- the same for every j.
   const int r0 = wave * kRowsPerLoad + (lane >> 3);
   const int dma_c = slot_of(r0, lane & 7);
-  const E* pa = static_cast<const E*>(a.A) + (static_cast<int64_t>(tile.row0) + r0) * N + dma_c * 8;
-  const E* pb =
-      static_cast<const E*>(a.B) + (static_cast<int64_t>(tile.g) * a.K + col0 + r0) * N + dma_c * 8;
-  uint32_t va = 0, vb = 0;   // bit j: load j's row lies inside the tile
-#pragma unroll
-  for (int j = 0; j < kLoadsA; ++j) va |= (r0 + kLoadRows * j < rows ? 1u : 0u) << j;
-#pragma unroll
-  for (int j = 0; j < kLoadsB; ++j) vb |= (r0 + kLoadRows * j < cols ? 1u : 0u) << j;
-  const void* zero = &kZero16;
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_offset(lds));
-  const int64_t row_step = kLoadRows * N;
+  const int64_t chunk_row0 = a.chunk_row0[a.chunk];
+  const uint32_t row_bytes = static_cast<uint32_t>(N * sizeof(E));
+  // byte offset of load j's row chunk within a tile's operand buffer (the
+  // same for d_y and weight rows)
+  uint32_t voff[kLoadsA];
+#pragma unroll
+  for (int j = 0; j < kLoadsA; ++j)
+    voff[j] = static_cast<uint32_t>(r0 + kLoadRows * j) * row_bytes + static_cast<uint32_t>(dma_c * 16);
 
-  auto issue = [&](int kt) {
-    const uint32_t base = lds0 + static_cast<uint32_t>((kt % kStages) * kStageSlots * 16);
-    const int64_t n0 = static_cast<int64_t>(kt) * kBK;
-    const bool in_n = n0 + dma_c * 8 < N;
+  auto operands = [&](int j) {
+    const int4 e = entry(j);
+    const int64_t col0 = a.k_lo + static_cast<int64_t>(e.w) * kBN;
+    const int cols = static_cast<int>(min<int64_t>(kBN, a.k_hi - col0));
+    Operands o;
+    o.a = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<E*>(static_cast<const E*>(a.A) + static_cast<int64_t>(e.y) * N), 0,
+        static_cast<int>(static_cast<uint32_t>(e.z) * row_bytes), 0x00020000);
+    o.b = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<E*>(static_cast<const E*>(a.B) + (static_cast<int64_t>(e.x) * a.K + col0) * N), 0,
+        static_cast<int>(static_cast<uint32_t>(cols) * row_bytes), 0x00020000);
+    return o;
+  };
+  // stage kt of a tile into LDS slot s; chunks past N read zeros
+  // (offsets stay below 2^31 in range, and below 2^32 from kOutside)
+  auto issue = [&](const Operands& o, int kt, int s) {
+    const uint32_t base = lds0 + static_cast<uint32_t>(s * kStageSlots * 16);
+    const uint32_t koff = static_cast<uint32_t>(kt) * kBK * sizeof(E);
+    const bool in_n = static_cast<int64_t>(kt) * kBK + dma_c * 8 < N;
 #pragma unroll
     for (int j = 0; j < kLoadsA; ++j)
-      dma16(in_n && ((va >> j) & 1) ? static_cast<const void*>(pa + j * row_step + n0) : zero,
-            base + static_cast<uint32_t>((j * kWaves + wave) * 64 * 16));
+      dma16_buf(o.a, (in_n ? voff[j] : kOutside) + koff,
+                base + static_cast<uint32_t>((j * kWaves + wave) * 64 * 16));
 #pragma unroll
     for (int j = 0; j < kLoadsB; ++j)
-      dma16(in_n && ((vb >> j) & 1) ? static_cast<const void*>(pb + j * row_step + n0) : zero,
-            base + static_cast<uint32_t>((kSlotsA + (j * kWaves + wave) * 64) * 16));
+      dma16_buf(o.b, (in_n ? voff[j] : kOutside) + koff,
+                base + static_cast<uint32_t>((kSlotsA + (j * kWaves + wave) * 64) * 16));
   };
-
   // fragment rows start at multiples of 32, so (row >> 1) & 7 == (lr >> 1) & 7
-  auto load_frags = [&](int kt, int q, u32x4_t (&fa)[kFM], u32x4_t (&fb)[kFN]) {
-    const u32x4_t* st = lds + (kt % kStages) * kStageSlots;
+  auto load_frags = [&](int s, int q, u32x4_t (&fa)[kFM], u32x4_t (&fb)[kFN]) {
+    const u32x4_t* st = lds + s * kStageSlots;
     const int sl = slot_of(lr, 2 * q + lh);
 #pragma unroll
     for (int i = 0; i < kFM; ++i) fa[i] = st[(wm * kWTM + i * 32 + lr) * kRowChunks + sl];
@@ -142,12 +211,6 @@ void produce_large_kernel(LargeArgs a) {
     for (int j = 0; j < kFN; ++j) fb[j] = st[kSlotsA + (wn * kWTN + j * 32 + lr) * kRowChunks + sl];
   };
   f32x16_t acc[kFM][kFN];
-#pragma unroll
-  for (int i = 0; i < kFM; ++i)
-#pragma unroll
-    for (int j = 0; j < kFN; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
   auto mfmas = [&](const u32x4_t (&fa)[kFM], const u32x4_t (&fb)[kFN]) {
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -158,70 +221,106 @@ void produce_large_kernel(LargeArgs a) {
   };
 
   const int nk = static_cast<int>((N + kBK - 1) / kBK);
-#pragma unroll
-  for (int s = 0; s < kStages; ++s)
-    if (s < nk) issue(s);
+  Operands oc = operands(cur);
+  Operands on = nxt < n_mine ? operands(nxt) : oc;
+  // stage d of the stream counted from the current tile's first stage: the
+  // current tile's, or -- past its last -- the next tile's, into LDS slot
+  // (d + par) & 1.  d <= nk + 1 < 2 nk, since the host runs this kernel only
+  // for nk >= 2, so the stream never reaches past the next tile.
+  auto issue_stream = [&](int d, int par) {
+    if (d < nk) issue(oc, d, (d + par) & 1);
+    else if (nxt < n_mine) issue(on, d - nk, (d + par) & 1);
+  };
+  int par = 0;   // LDS slot of the current tile's stage 0
+  issue_stream(0, par);
+  issue_stream(1, par);   // nk > 1 (the host's choice of this kernel), so stage 1 exists
   u32x4_t fa0[kFM], fb0[kFN], fa1[kFM], fb1[kFN];
-  // stage 0 landed (stage 1, if any, may still be in flight)
-  if (nk > 1) wait_then_barrier<kLoadsPerStage>(); else wait_then_barrier<0>();
-  load_frags(0, 0, fa0, fb0);
-  int kt = 0;
-  // steady state, free of branches so the compiler's LDS wait counts stay exact
-  for (; kt + kStages < nk; ++kt) {
+  // stage 0 landed (stage 1 may still be in flight)
+  wait_then_barrier<kLoadsPerStage>();
+  load_frags(par, 0, fa0, fb0);
+  for (;;) {
 #pragma unroll
-    for (int q = 0; q < kPairs; ++q) {
-      if (q + 1 < kPairs) {
-        if (q & 1) load_frags(kt, q + 1, fa0, fb0); else load_frags(kt, q + 1, fa1, fb1);
-      } else {
-        // stage kt+1 landed everywhere and every wave is done with stage kt;
-        // the refill of stage kt's buffer is issued by the first wave of each
-        // SIMD before its last MFMAs of the stage and by the second after
-        // them, so one of the two is always feeding the matrix unit
-        wait_then_barrier<0>();
-        if (wave < kWaves / 2) issue(kt + kStages);
-        load_frags(kt + 1, 0, fa0, fb0);
-      }
-      if (q & 1) mfmas(fa1, fb1); else mfmas(fa0, fb0);
-      if (q + 1 == kPairs && wave >= kWaves / 2) issue(kt + kStages);
-    }
-  }
-  // last stages: nothing more to issue
-  for (; kt < nk; ++kt) {
+    for (int i = 0; i < kFM; ++i)
 #pragma unroll
-    for (int q = 0; q < kPairs; ++q) {
-      if (q + 1 < kPairs) {
-        if (q & 1) load_frags(kt, q + 1, fa0, fb0); else load_frags(kt, q + 1, fa1, fb1);
-      } else if (kt + 1 < nk) {
-        wait_then_barrier<0>();
-        load_frags(kt + 1, 0, fa0, fb0);
+      for (int j = 0; j < kFN; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+    const bool more = nxt < n_mine;
+    for (int kt = 0; kt < nk; ++kt) {
+      const int s = (kt + par) & 1;
+      const bool boundary = kt + 1 < nk || more;   // a next stage exists in the stream
+#pragma unroll
+      for (int q = 0; q < kPairs; ++q) {
+        if (q + 1 < kPairs) {
+          if (q & 1) load_frags(s, q + 1, fa0, fb0); else load_frags(s, q + 1, fa1, fb1);
+        } else if (boundary) {
+          // the stream's next stage landed everywhere and every wave is done
+          // with this one; its slot is refilled with the stage two ahead by
+          // the first wave of each SIMD before its last MFMAs of the stage and
+          // by the second after them, so one of the two is always feeding the
+          // matrix unit
+          wait_then_barrier<0>();
+          if (wave < kWaves / 2) issue_stream(kt + 2, par);
+          load_frags(s ^ 1, 0, fa0, fb0);
+        }
+        if (q & 1) mfmas(fa1, fb1); else mfmas(fa0, fb0);
+        if (q + 1 == kPairs && boundary && wave >= kWaves / 2) issue_stream(kt + 2, par);
       }
-      if (q & 1) mfmas(fa1, fb1); else mfmas(fa0, fb0);
     }
-  }
 
-  // Epilogue: accumulator v of lane (lr, lh) is row 8*(v/4) + 4*lh + v%4,
-  // column lr of its 32x32 block.
-  const int64_t ring_row0 = static_cast<int64_t>(tile.row0) - a.chunk_row0[a.chunk];
-  float* __restrict__ out = a.ring + ring_row0 * a.ldc + (col0 - a.k_lo);
-  const bool full = rows == kBM && cols == kBN;
+    // Epilogue: accumulator v of lane (lr, lh) is row 8*(v/4) + 4*lh + v%4,
+    // column lr of its 32x32 block.  The stores go through a buffer resource
+    // that ends at the tile's last element, so rows past the tile's rows are
+    // dropped by the range check; lanes of columns past the tile's columns
+    // get an offset outside it.
+    {
+      const int4 e = entry(cur);
+      const int rows = e.z;
+      const int64_t cofs = static_cast<int64_t>(e.w) * kBN;
+      const int cols = static_cast<int>(min<int64_t>(kBN, a.k_hi - a.k_lo - cofs));
+      const uint32_t ld4 = static_cast<uint32_t>(a.ldc) * 4u;   // ring row bytes
+      const __amdgpu_buffer_rsrc_t out = __builtin_amdgcn_make_buffer_rsrc(
+          a.ring + (static_cast<int64_t>(e.y) - chunk_row0) * a.ldc + cofs, 0,
+          static_cast<int>(static_cast<uint32_t>(rows - 1) * ld4 + static_cast<uint32_t>(cols) * 4u),
+          0x00020000);
+      const uint32_t lane_off = static_cast<uint32_t>(wm * kWTM + 4 * lh) * ld4;
 #pragma unroll
-  for (int i = 0; i < kFM; ++i)
+      for (int j = 0; j < kFN; ++j) {
+        const int n = wn * kWTN + j * 32 + lr;
+        // r * ld4 < 2^31 (256 rows of fewer than 2^21 floats): no wrap from kOutside
+        const uint32_t voff = n < cols ? lane_off + static_cast<uint32_t>(n) * 4u : kOutside;
 #pragma unroll
-    for (int j = 0; j < kFN; ++j) {
-      const int n = wn * kWTN + j * 32 + lr;
+        for (int i = 0; i < kFM; ++i)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int m = wm * kWTM + i * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
-        if (full || (m < rows && n < cols))
-          out[static_cast<int64_t>(m) * a.ldc + n] = acc[i][j][v];
+          for (int v = 0; v < 16; ++v) {
+            const uint32_t r = static_cast<uint32_t>(i * 32 + 8 * (v >> 2) + (v & 3));
+            // a scalar copy first: a bit-cast of the vector element itself
+            // compiles to element 0 whatever v is
+            const float x = acc[i][j][v];
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x), out, voff + r * ld4,
+                                                  0, 0);
+          }
       }
     }
+    if (!more) break;
+    // the next tile becomes current; its first stage sits in slot par ^ (nk & 1)
+    par = (par + nk) & 1;
+    cur = nxt;
+    oc = on;
+    nxt = next_tile(cur + 1);
+    if (nxt < n_mine) on = operands(nxt);
+  }
 }
 
 }  // namespace
 
+// The tile stream needs at least two stages per tile (N > kBK), and a tile's
+// operand rows and ring rows must each span less than 2^31 bytes (256 N
+// elements, 256 ring rows of panel_cols floats); other shapes take the
+// register-staged tile.
 bool produce_uses_dma(const Plan& p, bool aligned) {
-  return aligned && p.regime == kLarge && p.dtype != PGG_F32;
+  return aligned && p.regime == kLarge && p.dtype != PGG_F32 && p.N > kBK &&
+         p.N < (int64_t(1) << 22) && p.panel_cols < (int64_t(1) << 21);
 }
 
 hipError_t launch_produce_dma(const Plan& p, int chunk, int panel, const void* grad_y,
@@ -240,12 +339,21 @@ hipError_t launch_produce_dma(const Plan& p, int chunk, int panel, const void* g
   a.chunk = chunk;
   a.tc = p.tc;
   a.n_col_tiles = p.n_col_tiles;
-  unsigned tiles = static_cast<unsigned>(p.tc) * static_cast<unsigned>(p.n_col_tiles);
-  tiles = (tiles + kXcds * kSuper - 1) / (kXcds * kSuper) * (kXcds * kSuper);   // whole raster rounds
+  if (!produce_uses_dma(p, true)) return hipErrorInvalidValue;
+  // raster positions in whole rounds; one workgroup per compute unit, more
+  // (whole rounds) only when a workgroup's tile table would overflow
+  const int64_t span = (int64_t(p.tc) * p.n_col_tiles + kRound - 1) / kRound * kRound;
+  if (span >= (int64_t(1) << 30)) return hipErrorInvalidValue;
+  a.span = static_cast<int32_t>(span);
+  int64_t grid = std::min<int64_t>(span, kRound);
+  const int64_t need = (span + kMaxTilesPerWg - 1) / kMaxTilesPerWg;
+  if (grid < need) grid = (need + kRound - 1) / kRound * kRound;
   if (p.dtype == PGG_BF16)
-    hipLaunchKernelGGL(produce_large_kernel<TBf16>, dim3(tiles), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(produce_large_kernel<TBf16>, dim3(static_cast<unsigned>(grid)), dim3(kThreads),
+                       0, s, a);
   else
-    hipLaunchKernelGGL(produce_large_kernel<TF16>, dim3(tiles), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(produce_large_kernel<TF16>, dim3(static_cast<unsigned>(grid)), dim3(kThreads),
+                       0, s, a);
   return hipGetLastError();
 }
 
