@@ -63,7 +63,7 @@ def measured_traffic(kernel, workload):
                 h.update(f.read())
     except OSError:
         return None
-    e = table.get(kernel)
+    e = table.get(f"{kernel}@{workload}") or table.get(kernel)
     if not e or e.get("workload") != workload or e.get("sources_sha") != h.hexdigest()[:16]:
         return None
     return e["traffic_bytes_per_launch"]
@@ -683,7 +683,8 @@ def main():
                                               "kernels_ms_per_step",
                                               "kernels_event_bracketed_ms_per_step",
                                               "workspace_bytes", "ring_bytes",
-                                              "d_expanded_x_fp32_bytes", "plan")}
+                                              "d_expanded_x_fp32_bytes", "workspace_vs_MK4",
+                                              "plan")}
     for k in ("forward", "dweight", "routing", "unpermute"):
         if k in primary:
             line[k] = primary[k]
@@ -695,7 +696,8 @@ def main():
                                                "frac_bf16_peak", "roofline", "kernels_ms_per_step",
                                                "kernels_event_bracketed_ms_per_step",
                                                "workspace_bytes", "ring_bytes",
-                                               "d_expanded_x_fp32_bytes", "config", "dtype")}
+                                               "d_expanded_x_fp32_bytes", "workspace_vs_MK4",
+                                               "config", "dtype", "plan")}
         if "cpu_baseline" in large:
             line["large"]["cpu_baseline"] = large["cpu_baseline"]
         for k in ("forward", "dweight", "routing", "unpermute"):
