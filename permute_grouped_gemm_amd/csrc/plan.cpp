@@ -55,8 +55,28 @@ int64_t tiles_per_chunk(int bm, int64_t cols, size_t budget, int64_t max_tiles) 
 //    about 5 TB/s by ring row (more chunks);
 //  - every panel past the first reads d_y again: about 15 TB/s of extra
 //    reads for the 16-bit producers, which hide most of it behind the
-//    multiply, and 4.7 TB/s for the fp32 producer.
+//    multiply, and 4.7 TB/s for the fp32 producer;
+//  - the 16-bit large-tile producer runs one 256 x 256 tile per compute unit
+//    at a time, so a launch of T tiles takes ceil(T / 256) rounds of about
+//    21 us + 0.022 us x N each (measured at N = 2048 and 4096).  Rounds are
+//    counted at the m-tile bound (M / 256 plus one partial tile per expert),
+//    cut into chunks of the plan's size: the true count is known only on the
+//    device, and an estimate that is a few tiles short can hide a whole
+//    round per launch.
 // The weight-streaming producer keeps one panel.
+// Rounds of the 16-bit large-tile producer over all panels of width w with
+// chunks of tc m-tiles, at the m-tile bound max_tiles.
+int64_t producer_rounds(const Plan& q, int64_t w, int64_t tc, int64_t max_tiles) {
+  constexpr int64_t kCUs = 256;
+  int64_t rounds = 0;
+  for (int64_t k0 = 0; k0 < q.K; k0 += w) {
+    const int64_t ct = (std::min<int64_t>(w, q.K - k0) + q.bn - 1) / q.bn;
+    for (int64_t left = max_tiles; left > 0; left -= tc)
+      rounds += (std::min<int64_t>(left, tc) * ct + kCUs - 1) / kCUs;
+  }
+  return rounds;
+}
+
 int choose_panels(const Plan& q, size_t budget, int64_t max_tiles) {
   // the weight sweep stores whole K-column ring rows: one panel, whatever the override
   if (q.regime == kStream) return 1;
@@ -74,6 +94,7 @@ int choose_panels(const Plan& q, size_t budget, int64_t max_tiles) {
   const double dy_bytes = double(q.M) * double(q.N) * elem;
   const double ring_bytes = double(q.M) * double(q.K) * 4.0;
   const double dx_bytes = double(q.batch) * double(q.K) * 4.0;
+  const double round_ps = 21.0e6 + 22.0e3 * double(q.N);   // one round of 256 x 256 tiles, in ps
   int best = 1;
   double best_time = 0.0;
   int64_t last_width = -1;
@@ -89,6 +110,7 @@ int choose_panels(const Plan& q, size_t budget, int64_t max_tiles) {
     double t = (ring_bytes + dx_bytes * (2.0 * e - 1.0)) /
                (chunks <= kFewChunks ? kConsumeRate : kRowConsumeRate);
     t += double(panels - 1) * dy_bytes / reread_rate;
+    if (q.regime == kLarge) t += double(producer_rounds(q, w, tc, max_tiles)) * round_ps;
     if (n == 1 || t < best_time) {
       best = static_cast<int>(panels);
       best_time = t;

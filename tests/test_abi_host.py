@@ -144,6 +144,36 @@ def test_panel_override_keeps_weight_streaming_in_one_panel(monkeypatch):
     assert p["panel_cols"] == 1024 and p["n_panels"] == 7
 
 
+def _producer_rounds(p, K):
+    # rounds of 256 tiles of 256 x 256 per launch, at the plan's m-tile bound
+    rounds = 0
+    for k0 in range(0, K, p["panel_cols"]):
+        ct = -(-min(p["panel_cols"], K - k0) // 256)
+        left = p["max_tiles"]
+        while left > 0:
+            take = min(left, p["tiles_per_chunk"])
+            rounds += -(-take * ct // 256)
+            left -= take
+    return rounds
+
+
+def test_planner_counts_large_tile_producer_rounds(monkeypatch):
+    # the mid bf16 shape: 3 panels of 2560 columns give launches of 800 tiles
+    # at the m-tile bound (4 rounds for 3.1 rounds of work); the planner now
+    # picks a cut with fewer rounds.  The large fp16 shape keeps 7 panels x 2
+    # chunks (more panels or chunks cost the consumer more than they save)
+    monkeypatch.delenv("PGG_PANEL_COLS", raising=False)
+    mid = pgg.plan_desc(desc(M=16384, N=4096, G=16, K=7168, batch=2048, topk=8, dy=BF16))
+    assert mid["regime"] == 0
+    monkeypatch.setenv("PGG_PANEL_COLS", "2560")
+    three = pgg.plan_desc(desc(M=16384, N=4096, G=16, K=7168, batch=2048, topk=8, dy=BF16))
+    assert three["n_panels"] == 3
+    assert _producer_rounds(mid, 7168) < _producer_rounds(three, 7168)
+    monkeypatch.delenv("PGG_PANEL_COLS")
+    large = pgg.plan_desc(desc(M=110592, N=2048, G=60, K=7168, batch=13824, topk=8, dy=F16))
+    assert large["n_panels"] == 7 and large["panel_cols"] == 1024 and large["max_chunks"] == 2
+
+
 def test_noalloc_rejects_problems_beyond_its_scratch_before_any_hip_call():
     # the allocation-free entry point plans into a fixed 64 MiB scratch; index
     # tables that alone exceed it are refused on the host (fake pointers are
