@@ -648,7 +648,7 @@ def main():
                     help="only time hipBLASLt (torch.mm) on the large workload's per-chunk dense GEMM")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not supported",
+        print(f"bench.py: the library runs on exactly one GPU; --gpus {args.gpus} is not supported",
               file=sys.stderr)
         return 2
 

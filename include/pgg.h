@@ -44,7 +44,7 @@ typedef enum { PGG_F32 = 0, PGG_F16 = 1, PGG_BF16 = 2 } pgg_dtype;
 typedef enum {
   PGG_OK = 0,
   PGG_ERR_INVALID_ARG = 1,          /* a constraint of §1.2 / §2.3 is violated, or a NULL pointer */
-  PGG_ERR_UNSUPPORTED = 2,          /* valid per the page but beyond this build (e.g. M >= 2^31) */
+  PGG_ERR_UNSUPPORTED = 2,          /* valid per the page but beyond this library (e.g. M >= 2^31) */
   PGG_ERR_WORKSPACE_TOO_SMALL = 3,  /* workspace_bytes below pgg_moe_dx_workspace_size */
   PGG_ERR_HIP = 4,                  /* a HIP runtime call failed */
   PGG_ERR_MISALIGNED = 5            /* workspace not 256-byte aligned, or an input / output pointer
