@@ -216,6 +216,24 @@ def test_row_shuffle_inside_groups_integer(orc):
     np.testing.assert_array_equal(bits(run(shuffled)), bits(run(case)))
 
 
+@pytest.mark.parametrize("kw", [
+    dict(batch=16, topk=8, G=16, K=2048, N=1024, dtype="bf16", empty=(1, 5, 9)),   # weight sweep
+    dict(batch=600, topk=8, G=9, K=2000, N=512, dtype="f16"),                     # large tiles
+    dict(batch=200, topk=4, G=5, K=600, N=264, dtype="f32"),                       # fp32 tiles
+    dict(batch=100, topk=3, G=4, K=700, N=286, dtype="bf16"),                      # unaligned rows
+], ids=["sweep", "large", "f32", "unaligned"])
+def test_power_of_two_scaling_bitwise(kw):
+    # multiplying d_y by 4 multiplies every product and every partial sum by 4
+    # exactly (random values, far from overflow and from the subnormals), so
+    # d_x is 4 times the first result bit for bit, whatever order the sums take
+    case = synth.make_case(seed=403, w_std=0.02, **kw)
+    base = run(case)
+    gy, w, eri, gl = upload(case)
+    gy.mul_(4)
+    got = run(case, tensors=(gy, w, eri, gl))
+    np.testing.assert_array_equal(bits(got), bits(base * 4))
+
+
 @pytest.mark.parametrize("which", ["tiny", "stream", "large", "chunked"])
 def test_ten_runs_bit_identical(orc, which, monkeypatch):
     if which == "tiny":
