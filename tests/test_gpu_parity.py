@@ -252,6 +252,30 @@ def test_ten_runs_bit_identical(orc, which, monkeypatch):
         np.testing.assert_array_equal(bits(run(case, tensors=tensors)), bits(first))
 
 
+def test_concurrent_calls_on_two_streams():
+    # calls share nothing but the inputs they are given: two problems (weight
+    # sweep and large tiles) enqueued alternately on two streams, each with
+    # its own workspace and output, give exactly their one-at-a-time results
+    cases = [synth.make_case(16, 8, 16, 2048, 1024, "bf16", seed=503, empty=(2, 7)),
+             synth.make_case(1024, 8, 8, 1024, 512, "f16", seed=504, w_std=0.02)]
+    tensors = [upload(c) for c in cases]
+    alone = [run(c, tensors=t) for c, t in zip(cases, tensors)]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    ws, outs = [], []
+    for c, t in zip(cases, tensors):
+        ws.append(torch.empty(pgg.workspace_size(*t, c.batch, c.topk, c.row_idx_type),
+                              dtype=torch.uint8, device="cuda"))
+        outs.append(torch.full((c.batch, c.K), float("nan"), dtype=torch.float32, device="cuda"))
+    torch.cuda.synchronize()
+    for _ in range(3):
+        for c, t, w, o, s in zip(cases, tensors, ws, outs, streams):
+            pgg.moe_dx(*t, c.batch, c.topk, c.row_idx_type, out=o, workspace=w, stream=s)
+    torch.cuda.synchronize()
+    for c, w, o, want in zip(cases, ws, outs, alone):
+        assert pgg.read_device_error(w) == (pgg.DEV_OK, 0)
+        np.testing.assert_array_equal(bits(o.cpu().numpy()), bits(want))
+
+
 # ---------------------------------------------------------------- device error word
 
 def _err(case):
