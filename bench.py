@@ -430,7 +430,9 @@ def measure(name, steps, warmup, cpu_baseline, log, forward=True, cold_variant=N
     sclk = smi_sclk()
 
     flops, bytes_, producer_bytes = algorithmic(case)
-    prod_name = {0: "produce_large", 1: "produce_stream", 2: "produce_f32"}[plan["regime"]]
+    # the library's launch names: fp32 producers are "produce_f32" whatever the tile
+    prod_name = ("produce_f32" if case.dtype == "f32" else
+                 {0: "produce_large", 1: "produce_stream", 2: "produce_f32"}[plan["regime"]])
     hbm_bound = plan["regime"] == 1
     if hbm_bound:
         # algorithmic bytes of one launch: d_y and the non-empty experts' weights

@@ -5,9 +5,10 @@
 // (MoeInitRoutingGroupedMatmulGrad design page, §数学定义和公式 Step 1; the
 // page's cube output type is fp32 whatever the input type, §2.6.2), for the
 // m-tiles of one chunk, written into that chunk's fp32 ring rows.  This file
-// holds the general register-staged tile (fp32 inputs, and 16-bit inputs whose
-// rows are not 16-byte aligned); aligned 16-bit inputs take the direct-to-LDS
-// 256x256 tile or, with few rows per expert, the weight sweep.
+// holds the general register-staged tile: 128x128 for fp32 inputs with few
+// rows per expert, 256x256 for rows that are not 16-byte aligned.  Aligned
+// rows with many rows per expert take the direct-to-LDS 256x256 tile (every
+// input type), and 16-bit inputs with few rows per expert the weight sweep.
 //
 // Both operands are contiguous along the reduction index n: a d_y row and a
 // W[g] row (one output column) are each a run of N elements.  That is the
@@ -228,6 +229,7 @@ hipError_t launch_typed(const Plan& p, const GemmArgs& args, bool aligned, hipSt
 }  // namespace
 
 const char* produce_kernel_name(const Plan& p) {
+  if (p.dtype == PGG_F32) return "produce_f32";
   switch (p.regime) {
     case kLarge: return "produce_large";
     case kStream: return "produce_stream";
@@ -260,7 +262,9 @@ hipError_t launch_produce(const Plan& p, int chunk, int panel, const void* grad_
   switch (p.dtype) {
     case PGG_BF16: return launch_typed<TBf16>(p, args, aligned, s);
     case PGG_F16: return launch_typed<TF16>(p, args, aligned, s);
-    default: return launch_cfg<TF32, 128, 128, 2, 2>(p, args, aligned, s);
+    default:
+      return p.regime == kLarge ? launch_cfg<TF32, 256, 256, 2, 2>(p, args, aligned, s)
+                                : launch_cfg<TF32, 128, 128, 2, 2>(p, args, aligned, s);
   }
 }
 

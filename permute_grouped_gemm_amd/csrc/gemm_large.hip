@@ -1,8 +1,11 @@
-// Producer for many rows per expert (fp16 / bf16): the grouped-matmul
-// gradient C[i, k] = sum_n d_y[i, n] * W[g(i), k, n] with fp32 accumulation
-// (MoeInitRoutingGroupedMatmulGrad design page, §数学定义和公式 Step 1; fp32
-// cube output, §2.6.2) on 256x256 output tiles, written into the chunk's ring
-// rows.
+// Producer for many rows per expert (fp16 / bf16 / fp32, 16-byte aligned
+// rows): the grouped-matmul gradient C[i, k] = sum_n d_y[i, n] * W[g(i), k, n]
+// with fp32 accumulation (MoeInitRoutingGroupedMatmulGrad design page,
+// §数学定义和公式 Step 1; fp32 cube output, §2.6.2) on 256x256 output tiles,
+// written into the chunk's ring rows.  fp32 inputs run the same tile: a
+// 16-byte chunk then holds 4 reduction elements instead of 8, so a stage
+// covers 32 of them, and each fragment pair feeds four 32x32x2 fp32 MFMAs
+// (sixteen times the MFMA time per stage against the same loads).
 //
 // Persistent: one workgroup per compute unit walks the launch's tiles
 // t = blockIdx.x + j * gridDim.x in the XCD super-block raster (raster<8,4>;
@@ -15,7 +18,7 @@
 // drain while it multiplies.
 //
 // Operand staging is direct buffer -> LDS (buffer_load_dwordx4 ... lds: lane
-// i's 16 bytes land at M0 + 16 i), two stages of 64 reduction elements (64 KiB
+// i's 16 bytes land at M0 + 16 i), two stages of 128 bytes per row (64 KiB
 // each: 256 d_y rows + 256 weight rows of 128 bytes, whole cache lines).  The
 // loads are issued by inline assembly so the compiler does not serialise them
 // with a blanket wait before every LDS read; the waits on their counter are
@@ -55,7 +58,9 @@ constexpr int kWM = 2;                        // waves along rows
 constexpr int kWTM = 128, kWTN = 64;          // wave tile
 constexpr int kFM = kWTM / 32, kFN = kWTN / 32;
 constexpr int kRowChunks = 8;                 // 16-byte chunks per LDS row per stage
-constexpr int kBK = kRowChunks * 8;           // reduction elements per stage
+// reduction elements per stage: 128 bytes of each row
+template <class T>
+constexpr int stage_elems() { return kRowChunks * T::kPerChunk; }
 constexpr int kPairs = kRowChunks / 2;
 constexpr int kStages = 2;
 constexpr int kSlotsA = kBM * kRowChunks;
@@ -115,6 +120,7 @@ template <class T>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void produce_large_kernel(LargeArgs a) {
   using E = typename T::elem;
+  constexpr int kBK = stage_elems<T>();
   __shared__ u32x4_t lds[kStages * kStageSlots];
   // this workgroup's tiles: {g, row0, rows, column tile}; rows 0 = no tile
   __shared__ int4 tab[kMaxTilesPerWg];
@@ -192,8 +198,8 @@ void produce_large_kernel(LargeArgs a) {
   // (offsets stay below 2^31 in range, and below 2^32 from kOutside)
   auto issue = [&](const Operands& o, int kt, int s) {
     const uint32_t base = lds0 + static_cast<uint32_t>(s * kStageSlots * 16);
-    const uint32_t koff = static_cast<uint32_t>(kt) * kBK * sizeof(E);
-    const bool in_n = static_cast<int64_t>(kt) * kBK + dma_c * 8 < N;
+    const uint32_t koff = static_cast<uint32_t>(kt) * kRowChunks * 16u;
+    const bool in_n = static_cast<int64_t>(kt) * kBK + dma_c * T::kPerChunk < N;
 #pragma unroll
     for (int j = 0; j < kLoadsA; ++j)
       dma16_buf(o.a, (in_n ? voff[j] : kOutside) + koff,
@@ -338,12 +344,13 @@ void produce_large_kernel(LargeArgs a) {
 
 }  // namespace
 
-// The tile stream needs at least two stages per tile (N > kBK), and a tile's
+// The tile stream needs at least two stages per tile, and a tile's
 // operand rows and ring rows must each span less than 2^31 bytes (256 N
 // elements, 256 ring rows of panel_cols floats); other shapes take the
 // register-staged tile.
 bool produce_uses_dma(const Plan& p, bool aligned) {
-  return aligned && p.regime == kLarge && p.dtype != PGG_F32 && p.N > kBK &&
+  const int64_t bk = p.dtype == PGG_F32 ? stage_elems<TF32>() : stage_elems<TBf16>();
+  return aligned && p.regime == kLarge && p.N > bk &&
          p.N < (int64_t(1) << 22) && p.panel_cols < (int64_t(1) << 21);
 }
 
@@ -374,6 +381,9 @@ hipError_t launch_produce_dma(const Plan& p, int chunk, int panel, const void* g
   if (grid < need) grid = (need + kRound - 1) / kRound * kRound;
   if (p.dtype == PGG_BF16)
     hipLaunchKernelGGL(produce_large_kernel<TBf16>, dim3(static_cast<unsigned>(grid)), dim3(kThreads),
+                       0, s, a);
+  else if (p.dtype == PGG_F32)
+    hipLaunchKernelGGL(produce_large_kernel<TF32>, dim3(static_cast<unsigned>(grid)), dim3(kThreads),
                        0, s, a);
   else
     hipLaunchKernelGGL(produce_large_kernel<TF16>, dim3(static_cast<unsigned>(grid)), dim3(kThreads),

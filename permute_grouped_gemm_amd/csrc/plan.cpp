@@ -56,9 +56,10 @@ int64_t tiles_per_chunk(int bm, int64_t cols, size_t budget, int64_t max_tiles) 
 //  - every panel past the first reads d_y again: about 15 TB/s of extra
 //    reads for the 16-bit producers, which hide most of it behind the
 //    multiply, and 4.7 TB/s for the fp32 producer;
-//  - the 16-bit large-tile producer runs one 256 x 256 tile per compute unit
-//    at a time, so a launch of T tiles takes ceil(T / 256) rounds of about
-//    21 us + 0.022 us x N each (measured at N = 2048 and 4096).  Rounds are
+//  - the large-tile producer runs one 256 x 256 tile per compute unit at a
+//    time, so a launch of T tiles takes ceil(T / 256) rounds of about
+//    21 us + 0.022 us x N each for 16-bit inputs (measured at N = 2048 and
+//    4096), and about 16 times that per N for fp32 (the MFMA rate).  Rounds are
 //    counted at the m-tile bound (M / 256 plus one partial tile per expert),
 //    cut into chunks of the plan's size: the true count is known only on the
 //    device, and an estimate that is a few tiles short can hide a whole
@@ -94,7 +95,8 @@ int choose_panels(const Plan& q, size_t budget, int64_t max_tiles) {
   const double dy_bytes = double(q.M) * double(q.N) * elem;
   const double ring_bytes = double(q.M) * double(q.K) * 4.0;
   const double dx_bytes = double(q.batch) * double(q.K) * 4.0;
-  const double round_ps = 21.0e6 + 22.0e3 * double(q.N);   // one round of 256 x 256 tiles, in ps
+  // one round of 256 x 256 tiles, in ps (fp32: the MFMA rate is 16 times lower)
+  const double round_ps = 21.0e6 + (q.dtype == PGG_F32 ? 230.0e3 : 22.0e3) * double(q.N);
   int best = 1;
   double best_time = 0.0;
   int64_t last_width = -1;
@@ -119,9 +121,9 @@ int choose_panels(const Plan& q, size_t budget, int64_t max_tiles) {
   return best;
 }
 
-// Output tile per regime: large-M MFMA tiles; for few rows per expert, m-tiles
-// of 32 rows crossed with units of 16 weight rows that a persistent grid
-// streams in address order; fp32 tiles.
+// Output tile per regime: large-M MFMA tiles (every input type); for few rows
+// per expert, m-tiles of 32 rows crossed with units of 16 weight rows that a
+// persistent grid streams in address order (16-bit), or 128 x 128 tiles (fp32).
 TileShape tile_shape(int32_t regime) {
   switch (regime) {
     case kLarge: return {256, 256};
@@ -163,10 +165,10 @@ pgg_status plan_with_budget(const pgg_moe_dx_desc* d, size_t budget, Plan* p) {
   q.row_idx_type = d->row_idx_type;
   q.panel_cols = q.K;
   q.dtype = d->grad_y_dtype;
-  if (q.dtype == PGG_F32) {
-    q.regime = kF32;
-  } else if (M <= 64 * G) {
-    q.regime = kStream;   // on average at most 64 rows per expert: weight streaming dominates
+  if (M <= 64 * G) {
+    // on average at most 64 rows per expert: weight streaming dominates (fp32
+    // keeps its own 128 x 128 tile there)
+    q.regime = q.dtype == PGG_F32 ? kF32 : kStream;
   } else {
     q.regime = kLarge;
   }

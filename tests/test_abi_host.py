@@ -86,6 +86,11 @@ def test_ring_never_exceeds_the_intermediate():
 
 def test_plan_regimes():
     assert pgg.plan_desc(desc(dy=F32))["regime"] == 2
+    # fp32 with many rows per expert takes the 256 x 256 tiles of the 16-bit types
+    big32 = pgg.plan_desc(desc(M=110592, N=2048, G=60, K=7168, batch=13824, topk=8, dy=F32))
+    assert big32["regime"] == 0 and big32["block_m"] == 256 and big32["block_n"] == 256
+    few32 = pgg.plan_desc(desc(M=128, N=4096, G=16, K=7168, batch=16, topk=8, dy=F32))
+    assert few32["regime"] == 2 and few32["block_m"] == 128
     decode = pgg.plan_desc(desc(M=128, N=4096, G=16, K=7168, batch=16, topk=8, dy=BF16))
     assert decode["regime"] == 1 and decode["max_chunks"] == 1        # one chunk: pure slot order
     large = pgg.plan_desc(desc(M=110592, N=2048, G=60, K=7168, batch=13824, topk=8, dy=F16))

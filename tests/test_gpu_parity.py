@@ -62,6 +62,7 @@ EXACT_SHAPES = [
     dict(batch=600, topk=4, G=5, K=600, N=300),           # large tiles, row/col/reduction tails
     dict(batch=10, topk=3, G=4, K=178, N=286),            # unaligned rows (N*2 % 16 != 0)
     dict(batch=700, topk=4, G=5, K=1000, N=2040),         # large tiles, aligned rows, N % 64 != 0
+    dict(batch=600, topk=4, G=5, K=600, N=286),           # large tiles, unaligned rows: register staged
     dict(batch=32, topk=8, G=16, K=512, N=256, routing="heavy", empty=(3,), heavy=0,
          heavy_rows=50),                                    # streaming, one m-tile per pass, 4 passes
     dict(batch=64, topk=8, G=16, K=520, N=264, routing="heavy", empty=(3,), heavy=5,
