@@ -51,31 +51,53 @@ int64_t tiles_per_chunk(int bm, int64_t cols, size_t budget, int64_t max_tiles) 
 //    of a token's topK rows in any chunk alike, the token's rows fall in
 //    E = C (1 - (1 - 1/C)^topK) distinct chunks and its d_x row is read and
 //    written 2E - 1 times (once when C = 1); it moves these bytes at about
-//    6.7 TB/s when consuming by token (at most kFewChunks chunks) and at
-//    about 5 TB/s by ring row (more chunks);
+//    6.4-6.8 TB/s with up to 3 chunks per panel, about 5 TB/s with 4 (the
+//    chunk consumer) and about 5 TB/s by ring row (more chunks);
 //  - every panel past the first reads d_y again: about 15 TB/s of extra
 //    reads for the 16-bit producers, which hide most of it behind the
 //    multiply, and 4.7 TB/s for the fp32 producer;
 //  - the large-tile producer runs one 256 x 256 tile per compute unit at a
 //    time, so a launch of T tiles takes ceil(T / 256) rounds of about
 //    21 us + 0.022 us x N each for 16-bit inputs (measured at N = 2048 and
-//    4096), and about 16 times that per N for fp32 (the MFMA rate).  Rounds are
-//    counted at the m-tile bound (M / 256 plus one partial tile per expert),
-//    cut into chunks of the plan's size: the true count is known only on the
-//    device, and an estimate that is a few tiles short can hide a whole
-//    round per launch.
+//    4096), and about 16 times that per N for fp32 (the MFMA rate).  The
+//    true m-tile count is known only on the device; rounds are counted at
+//    its expectation under routing that is uniform over the experts
+//    (expected_tiles), cut into chunks of the plan's size (which the bound
+//    sets).  The bound (M / 256 plus one partial tile per every expert)
+//    overstates a launch by up to G / 2 m-tiles, which at 64 experts of
+//    about 512 rows (K 7168, N 2048) made 7 panels of one chunk look as fast
+//    as 2 panels of three, against 1.52 and 1.38 ms measured.
 // The weight-streaming producer keeps one panel.
-// Rounds of the 16-bit large-tile producer over all panels of width w with
-// chunks of tc m-tiles, at the m-tile bound max_tiles.
-int64_t producer_rounds(const Plan& q, int64_t w, int64_t tc, int64_t max_tiles) {
+// Rounds of the large-tile producer over all panels of width w with chunks
+// of tc m-tiles, for `tiles` m-tiles.
+int64_t producer_rounds(const Plan& q, int64_t w, int64_t tc, int64_t tiles) {
   constexpr int64_t kCUs = 256;
   int64_t rounds = 0;
   for (int64_t k0 = 0; k0 < q.K; k0 += w) {
     const int64_t ct = (std::min<int64_t>(w, q.K - k0) + q.bn - 1) / q.bn;
-    for (int64_t left = max_tiles; left > 0; left -= tc)
+    for (int64_t left = tiles; left > 0; left -= tc)
       rounds += (std::min<int64_t>(left, tc) * ct + kCUs - 1) / kCUs;
   }
   return rounds;
+}
+
+// Expected m-tiles of bm rows over the G experts when each token's topK
+// experts are distinct and uniform: an expert's row count is then
+// Binomial(batch, topK / G), and E[ceil(c / bm)] = sum_j P(c > j bm), taken
+// from the normal approximation with continuity correction.  Clamped to
+// [ceil(M / bm), max_tiles].
+int64_t expected_tiles(const Plan& q, int64_t max_tiles) {
+  const double p = std::min(1.0, double(q.topk) / double(q.G));
+  const double mu = double(q.batch) * p;
+  const double sd = std::sqrt(double(q.batch) * p * (1.0 - p));
+  double per_expert = 0.0;
+  for (int64_t j = 0; double(j) * q.bm < mu + 8.0 * sd + 1.0; ++j) {
+    const double x = double(j) * q.bm;
+    per_expert += sd > 0.0 ? 0.5 * std::erfc((x + 0.5 - mu) / (sd * std::sqrt(2.0))) : (mu > x ? 1.0 : 0.0);
+  }
+  const int64_t lo = (q.M + q.bm - 1) / q.bm;
+  const int64_t est = static_cast<int64_t>(std::ceil(per_expert * double(q.G)));
+  return std::max<int64_t>(lo, std::min<int64_t>(est, max_tiles));
 }
 
 int choose_panels(const Plan& q, size_t budget, int64_t max_tiles) {
@@ -89,7 +111,8 @@ int choose_panels(const Plan& q, size_t budget, int64_t max_tiles) {
       return static_cast<int>((q.K + w - 1) / w);
     }
   }
-  constexpr double kConsumeRate = 6.7, kRowConsumeRate = 5.0;
+  constexpr double kConsumeRate = 6.7, kManyChunkRate = 5.0;
+  constexpr int64_t kFastChunks = 3;
   const double reread_rate = q.dtype == PGG_F32 ? 4.7 : 15.0;
   const double elem = q.dtype == PGG_F32 ? 4.0 : 2.0;
   const double dy_bytes = double(q.M) * double(q.N) * elem;
@@ -97,6 +120,7 @@ int choose_panels(const Plan& q, size_t budget, int64_t max_tiles) {
   const double dx_bytes = double(q.batch) * double(q.K) * 4.0;
   // one round of 256 x 256 tiles, in ps (fp32: the MFMA rate is 16 times lower)
   const double round_ps = 21.0e6 + (q.dtype == PGG_F32 ? 230.0e3 : 22.0e3) * double(q.N);
+  const int64_t est_tiles = expected_tiles(q, max_tiles);
   int best = 1;
   double best_time = 0.0;
   int64_t last_width = -1;
@@ -110,9 +134,9 @@ int choose_panels(const Plan& q, size_t budget, int64_t max_tiles) {
     const double c = double(chunks);
     const double e = c * (1.0 - std::pow(1.0 - 1.0 / c, double(q.topk)));
     double t = (ring_bytes + dx_bytes * (2.0 * e - 1.0)) /
-               (chunks <= kFewChunks ? kConsumeRate : kRowConsumeRate);
+               (chunks <= kFastChunks ? kConsumeRate : kManyChunkRate);
     t += double(panels - 1) * dy_bytes / reread_rate;
-    if (q.regime == kLarge) t += double(producer_rounds(q, w, tc, max_tiles)) * round_ps;
+    if (q.regime == kLarge) t += double(producer_rounds(q, w, tc, est_tiles)) * round_ps;
     if (n == 1 || t < best_time) {
       best = static_cast<int>(panels);
       best_time = t;

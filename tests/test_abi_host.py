@@ -99,6 +99,20 @@ def test_plan_regimes():
     assert large["max_chunks"] * large["tiles_per_chunk"] >= large["max_tiles"]
 
 
+def test_panel_choice_at_measured_shapes():
+    # plans the time estimate picks where every panel width was timed on an
+    # MI355X (the default within 1 % of the best measured, or the best)
+    for m, g, n, k, dt, want in ((110592, 60, 2048, 7168, F16, 7),    # large fp16: 7 x 1024
+                                 (110592, 60, 2048, 7168, F32, 2),    # large fp32: 2 x 3584
+                                 (32768, 64, 2048, 7168, BF16, 2),    # 64 experts of ~512 rows
+                                 (65536, 32, 1536, 4096, BF16, 2),
+                                 (8192, 8, 14336, 4096, BF16, 1),
+                                 (55296, 60, 2048, 7168, F16, 4)):
+        topk = 2 if g == 8 else 8
+        p = pgg.plan_desc(desc(M=m, N=n, G=g, K=k, batch=m // topk, topk=topk, dy=dt))
+        assert p["n_panels"] == want, (m, g, n, k, p)
+
+
 def test_column_panels():
     # panels are whole tiles wide and cover K; the weight-streaming regime keeps one panel
     for m, g, n, k, topk, dt in ((128, 16, 4096, 7168, 8, BF16), (16384, 16, 4096, 7168, 8, BF16),
