@@ -5,6 +5,7 @@
 // the expert-ordered list of m-tiles into chunks whose fp32 output rows fit a
 // ring of bounded size, so the workspace does not grow with M·K.
 #include <stdlib.h>
+#include <string.h>
 
 #include <algorithm>
 #include <cmath>
@@ -81,23 +82,49 @@ int64_t producer_rounds(const Plan& q, int64_t w, int64_t tc, int64_t tiles) {
   return rounds;
 }
 
-// Expected m-tiles of bm rows over the G experts when each token's topK
-// experts are distinct and uniform: an expert's row count is then
-// Binomial(batch, topK / G), and E[ceil(c / bm)] = sum_j P(c > j bm), taken
-// from the normal approximation with continuity correction.  Clamped to
-// [ceil(M / bm), max_tiles].
-int64_t expected_tiles(const Plan& q, int64_t max_tiles) {
+// Expected m-tiles of bm rows per expert when each token's topK experts are
+// distinct and uniform: an expert's row count is then Binomial(batch, topK /
+// G), and E[ceil(c / bm)] = sum_j P(c > j bm), taken from the normal
+// approximation with continuity correction.
+double expected_tiles_per_expert(const Plan& q, int bm) {
   const double p = std::min(1.0, double(q.topk) / double(q.G));
   const double mu = double(q.batch) * p;
   const double sd = std::sqrt(double(q.batch) * p * (1.0 - p));
   double per_expert = 0.0;
-  for (int64_t j = 0; double(j) * q.bm < mu + 8.0 * sd + 1.0; ++j) {
-    const double x = double(j) * q.bm;
+  for (int64_t j = 0; double(j) * bm < mu + 8.0 * sd + 1.0; ++j) {
+    const double x = double(j) * bm;
     per_expert += sd > 0.0 ? 0.5 * std::erfc((x + 0.5 - mu) / (sd * std::sqrt(2.0))) : (mu > x ? 1.0 : 0.0);
   }
+  return per_expert;
+}
+
+// The same over all experts, clamped to [ceil(M / bm), max_tiles].
+int64_t expected_tiles(const Plan& q, int64_t max_tiles) {
   const int64_t lo = (q.M + q.bm - 1) / q.bm;
-  const int64_t est = static_cast<int64_t>(std::ceil(per_expert * double(q.G)));
+  const int64_t est = static_cast<int64_t>(std::ceil(expected_tiles_per_expert(q, q.bm) * double(q.G)));
   return std::max<int64_t>(lo, std::min<int64_t>(est, max_tiles));
+}
+
+// Producer family.  Measured on MI355X with uniform routing (K x N of 7168 x
+// 4096, 7168 x 2048 and 2048 x 1408; 16, 60 and 64 experts):
+//  - 16-bit: the weight sweep reads every expert's weights once per 32-row
+//    m-tile, the 256 x 256 tiles once per 256 rows.  The sweep is faster up
+//    to 24 rows per expert (197 against 236 us, 405 against 456 us) and the
+//    tiles from 32 (240 against 253 us, 473 against 534 us, 112 against 140
+//    us), so the sweep takes M <= 28 G.
+//  - fp32: both tiles are bound by the fp32 MFMAs, which also multiply the
+//    padding rows of each expert's last m-tile.  The large tile is taken
+//    when its expected padded rows take less time at relative rates of 0.85
+//    (256 x 256) and 0.78 (128 x 128), fitted to the measured choices: the
+//    large tile at 192 and 1024 rows per expert and at the large fp32 shape
+//    (1.95 against 2.19 ms, 16.05 against 16.51 ms, 25.4 against 27.4 ms),
+//    the small one at 32-128, 256, 384 and 512 (1.64 against 1.92 ms at 128,
+//    4.33 against 4.84 ms at 512).
+bool few_rows_per_expert(const Plan& q) {
+  if (q.dtype != PGG_F32) return q.M <= 28 * q.G;
+  const double t256 = expected_tiles_per_expert(q, 256) * 256.0 / 0.85;
+  const double t128 = expected_tiles_per_expert(q, 128) * 128.0 / 0.78;
+  return t128 <= t256;
 }
 
 int choose_panels(const Plan& q, size_t budget, int64_t max_tiles) {
@@ -189,12 +216,12 @@ pgg_status plan_with_budget(const pgg_moe_dx_desc* d, size_t budget, Plan* p) {
   q.row_idx_type = d->row_idx_type;
   q.panel_cols = q.K;
   q.dtype = d->grad_y_dtype;
-  if (M <= 64 * G) {
-    // on average at most 64 rows per expert: weight streaming dominates (fp32
-    // keeps its own 128 x 128 tile there)
-    q.regime = q.dtype == PGG_F32 ? kF32 : kStream;
-  } else {
-    q.regime = kLarge;
+  // few rows per expert: the weight sweep (16-bit) or the 128 x 128 tile (fp32)
+  q.regime = few_rows_per_expert(q) ? (q.dtype == PGG_F32 ? kF32 : kStream) : kLarge;
+  // PGG_REGIME=large or =few fixes the producer family (tuning)
+  if (const char* e = getenv("PGG_REGIME")) {
+    if (!strcmp(e, "large")) q.regime = kLarge;
+    else if (!strcmp(e, "few")) q.regime = q.dtype == PGG_F32 ? kF32 : kStream;
   }
   const TileShape ts = tile_shape(q.regime);
   q.bm = ts.bm;

@@ -99,6 +99,21 @@ def test_plan_regimes():
     assert large["max_chunks"] * large["tiles_per_chunk"] >= large["max_tiles"]
 
 
+def test_regime_choice_at_measured_shapes():
+    # producer family per rows per expert where both were timed on an MI355X
+    # (uniform routing, topK 8): regime 1 = weight sweep, 2 = fp32 128 x 128
+    # tiles, 0 = 256 x 256 tiles
+    for g, k, n, dt, per, want in ((16, 7168, 4096, BF16, 24, 1), (16, 7168, 4096, BF16, 32, 0),
+                                   (60, 7168, 2048, F16, 24, 1), (60, 7168, 2048, F16, 32, 0),
+                                   (64, 2048, 1408, BF16, 16, 1), (64, 2048, 1408, BF16, 32, 0),
+                                   (16, 7168, 4096, F32, 128, 2), (16, 7168, 4096, F32, 192, 0),
+                                   (16, 7168, 4096, F32, 512, 2), (60, 7168, 2048, F32, 512, 2),
+                                   (60, 7168, 2048, F32, 1024, 0)):
+        m = g * per
+        p = pgg.plan_desc(desc(M=m, N=n, G=g, K=k, batch=m // 8, topk=8, dy=dt))
+        assert p["regime"] == want, (g, k, n, dt, per, p)
+
+
 def test_panel_choice_at_measured_shapes():
     # plans the time estimate picks where every panel width was timed on an
     # MI355X (the default within 1 % of the best measured, or the best)
@@ -151,7 +166,7 @@ def test_panel_override_keeps_weight_streaming_in_one_panel(monkeypatch):
     # the weight sweep stores ring rows of all K columns, so a panel-width
     # override must not cut a weight-streaming plan into panels
     monkeypatch.setenv("PGG_PANEL_COLS", "1024")
-    for m, g, n, k, topk in ((128, 16, 4096, 7168, 8), (1024, 16, 4096, 7168, 8)):
+    for m, g, n, k, topk in ((128, 16, 4096, 7168, 8), (448, 16, 4096, 7168, 8)):
         p = pgg.plan_desc(desc(M=m, N=n, G=g, K=k, batch=m // topk, topk=topk, dy=BF16))
         assert p["regime"] == 1
         assert p["n_panels"] == 1 and p["panel_cols"] == k

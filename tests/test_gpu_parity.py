@@ -65,7 +65,7 @@ EXACT_SHAPES = [
     dict(batch=600, topk=4, G=5, K=600, N=286),           # large tiles, unaligned rows: register staged
     dict(batch=32, topk=8, G=16, K=512, N=256, routing="heavy", empty=(3,), heavy=0,
          heavy_rows=50),                                    # streaming, one m-tile per pass, 4 passes
-    dict(batch=64, topk=8, G=16, K=520, N=264, routing="heavy", empty=(3,), heavy=5,
+    dict(batch=56, topk=8, G=16, K=520, N=264, routing="heavy", empty=(3,), heavy=5,
          heavy_rows=100),                                   # streaming, two m-tiles per pass, K/N tails
     dict(batch=4, topk=2, G=4, K=5, N=8),                  # streaming: one partial unit, one tiny stage
     dict(batch=4, topk=2, G=4, K=40, N=24),                # streaming: K not a multiple of 16
@@ -98,7 +98,7 @@ def test_many_chunks_stream_bit_exact(orc, monkeypatch):
     # few rows per expert (weight-sweep producer) split over many chunks,
     # with one expert above 32 rows so its m-tiles straddle chunks
     monkeypatch.setenv("PGG_RING_MB", "1")
-    case = synth.make_case(64, 8, 16, 2048, 1024, "bf16", seed=203, integer=True, routing="heavy",
+    case = synth.make_case(56, 8, 16, 2048, 1024, "bf16", seed=203, integer=True, routing="heavy",
                            heavy=4, heavy_rows=60)
     gy, w, eri, gl = upload(case)
     plan = pgg.plan(gy, w, eri, gl, case.batch, case.topk, 0)
