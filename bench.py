@@ -430,9 +430,11 @@ def measure(name, steps, warmup, cpu_baseline, log, forward=True, cold_variant=N
     sclk = smi_sclk()
 
     flops, bytes_, producer_bytes = algorithmic(case)
-    # the library's launch names: fp32 producers are "produce_f32" whatever the tile
-    prod_name = ("produce_f32" if case.dtype == "f32" else
-                 {0: "produce_large", 1: "produce_stream", 2: "produce_f32"}[plan["regime"]])
+    # the library's launch names: the weight sweep is "produce_stream", the
+    # fp32 tiles "produce_f32" whatever their size
+    prod_name = ("produce_stream" if plan["regime"] == 1 else
+                 "produce_f32" if case.dtype == "f32" else
+                 {0: "produce_large", 2: "produce_f32"}[plan["regime"]])
     hbm_bound = plan["regime"] == 1
     if hbm_bound:
         # algorithmic bytes of one launch: d_y and the non-empty experts' weights

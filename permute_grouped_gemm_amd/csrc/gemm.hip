@@ -229,6 +229,7 @@ hipError_t launch_typed(const Plan& p, const GemmArgs& args, bool aligned, hipSt
 }  // namespace
 
 const char* produce_kernel_name(const Plan& p) {
+  if (p.regime == kStream) return "produce_stream";
   if (p.dtype == PGG_F32) return "produce_f32";
   switch (p.regime) {
     case kLarge: return "produce_large";

@@ -1,5 +1,5 @@
-// Producer for 16-bit inputs with few rows per expert: the same grouped-matmul
-// gradient as the tiled producers,
+// Producer for few rows per expert (bf16, fp16 and fp32 inputs): the same
+// grouped-matmul gradient as the tiled producers,
 //
 //   C[i, k] = sum_n d_y[i, n] * W[g(i), k, n]        (fp32 accumulate)
 //
@@ -17,10 +17,11 @@
 // spread their concurrent reads over the full tensor and read measurably
 // slower.
 //
-// A unit runs in stages of a fixed number of reduction elements per row.
-// Wave w multiplies the w-th quarter of every row of a stage with 16x16x32
-// MFMAs; at the end of a unit the four waves' partial sums are added in wave
-// order (fixed, so the result is bit-reproducible) and written to the ring.
+// A unit runs in stages of a fixed number of bytes per row.  Wave w
+// multiplies the w-th quarter of every row of a stage with 16x16x32 MFMAs
+// (16-bit) or 16x16x4 fp32 MFMAs; at the end of a unit the four waves'
+// partial sums are added in wave order (fixed, so the result is
+// bit-reproducible) and written to the ring.
 //
 // Rows that are 16-byte aligned take sweep_dma_kernel: stages of 512 bytes
 // per row; the weight slab (16 rows) and the tile's d_y rows (16 or 32) of a
@@ -97,6 +98,20 @@ template <>
 __device__ __forceinline__ void mma16<TF16>(f32x4_t& acc, u32x4_t a, u32x4_t b) {
   acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
                                                __builtin_bit_cast(f16x8_t, b), acc, 0, 0, 0);
+}
+
+// fp32: a chunk holds 4 reduction elements.  MFMA i takes element i of every
+// lane's chunk; lane group g supplies reduction slot g of both operands, and
+// both hold the same chunk there, so the four MFMAs cover the 16 elements of
+// the four chunks once each.
+template <>
+__device__ __forceinline__ void mma16<TF32>(f32x4_t& acc, u32x4_t a, u32x4_t b) {
+  const f32x4_t fa = __builtin_bit_cast(f32x4_t, a);
+  const f32x4_t fb = __builtin_bit_cast(f32x4_t, b);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[0], fb[0], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[1], fb[1], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[2], fb[2], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[3], fb[3], acc, 0, 0, 0);
 }
 
 // One unit's operands and output window.
@@ -527,6 +542,7 @@ hipError_t launch(const Plan& p, const SweepArgs& a, bool aligned, bool fused, h
   switch (p.dtype) {
     case PGG_BF16: return launch_typed<TBf16>(p, a, aligned, fused, s);
     case PGG_F16: return launch_typed<TF16>(p, a, aligned, fused, s);
+    case PGG_F32: return launch_typed<TF32>(p, a, aligned, fused, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -112,8 +112,12 @@ int64_t expected_tiles(const Plan& q, int64_t max_tiles) {
 //    to 24 rows per expert (197 against 236 us, 405 against 456 us) and the
 //    tiles from 32 (240 against 253 us, 473 against 534 us, 112 against 140
 //    us), so the sweep takes M <= 28 G.
-//  - fp32: both tiles are bound by the fp32 MFMAs, which also multiply the
-//    padding rows of each expert's last m-tile.  The large tile is taken
+//  - fp32 up to 48 rows per expert: the weight sweep (fp32 MFMAs on the same
+//    staged chunks) against the 128 x 128 tile, which is bound by its MFMAs
+//    on padding rows: 359 against 1057 us at 8 rows per expert, 606 against
+//    1070 at 32, 921 against 1078 at 48 (16 experts, 7168 x 4096).
+//  - fp32 above that: both tiles are bound by the fp32 MFMAs, which also
+//    multiply the padding rows of each expert's last m-tile.  The large tile is taken
 //    when its expected padded rows take less time at relative rates of 0.85
 //    (256 x 256) and 0.78 (128 x 128), fitted to the measured choices: the
 //    large tile at 192 and 1024 rows per expert and at the large fp32 shape
@@ -122,6 +126,7 @@ int64_t expected_tiles(const Plan& q, int64_t max_tiles) {
 //    4.33 against 4.84 ms at 512).
 bool few_rows_per_expert(const Plan& q) {
   if (q.dtype != PGG_F32) return q.M <= 28 * q.G;
+  if (q.M <= 48 * q.G) return true;   // the fp32 weight sweep
   const double t256 = expected_tiles_per_expert(q, 256) * 256.0 / 0.85;
   const double t128 = expected_tiles_per_expert(q, 128) * 128.0 / 0.78;
   return t128 <= t256;
@@ -174,7 +179,8 @@ int choose_panels(const Plan& q, size_t budget, int64_t max_tiles) {
 
 // Output tile per regime: large-M MFMA tiles (every input type); for few rows
 // per expert, m-tiles of 32 rows crossed with units of 16 weight rows that a
-// persistent grid streams in address order (16-bit), or 128 x 128 tiles (fp32).
+// persistent grid streams in address order; for fp32 in between, 128 x 128
+// tiles.
 TileShape tile_shape(int32_t regime) {
   switch (regime) {
     case kLarge: return {256, 256};
@@ -216,12 +222,16 @@ pgg_status plan_with_budget(const pgg_moe_dx_desc* d, size_t budget, Plan* p) {
   q.row_idx_type = d->row_idx_type;
   q.panel_cols = q.K;
   q.dtype = d->grad_y_dtype;
-  // few rows per expert: the weight sweep (16-bit) or the 128 x 128 tile (fp32)
-  q.regime = few_rows_per_expert(q) ? (q.dtype == PGG_F32 ? kF32 : kStream) : kLarge;
-  // PGG_REGIME=large or =few fixes the producer family (tuning)
+  // few rows per expert: the weight sweep, or for fp32 between the sweep and
+  // the large tile the 128 x 128 tile
+  if (!few_rows_per_expert(q)) q.regime = kLarge;
+  else if (q.dtype == PGG_F32 && q.M > 48 * q.G) q.regime = kF32;
+  else q.regime = kStream;
+  // PGG_REGIME=large, =few or =sweep fixes the producer family (tuning)
   if (const char* e = getenv("PGG_REGIME")) {
     if (!strcmp(e, "large")) q.regime = kLarge;
     else if (!strcmp(e, "few")) q.regime = q.dtype == PGG_F32 ? kF32 : kStream;
+    else if (!strcmp(e, "sweep")) q.regime = kStream;
   }
   const TileShape ts = tile_shape(q.regime);
   q.bm = ts.bm;

@@ -85,12 +85,15 @@ def test_ring_never_exceeds_the_intermediate():
 
 
 def test_plan_regimes():
-    assert pgg.plan_desc(desc(dy=F32))["regime"] == 2
+    # fp32 with 32 rows per expert: the weight sweep
+    assert pgg.plan_desc(desc(dy=F32))["regime"] == 1
     # fp32 with many rows per expert takes the 256 x 256 tiles of the 16-bit types
     big32 = pgg.plan_desc(desc(M=110592, N=2048, G=60, K=7168, batch=13824, topk=8, dy=F32))
     assert big32["regime"] == 0 and big32["block_m"] == 256 and big32["block_n"] == 256
     few32 = pgg.plan_desc(desc(M=128, N=4096, G=16, K=7168, batch=16, topk=8, dy=F32))
-    assert few32["regime"] == 2 and few32["block_m"] == 128
+    assert few32["regime"] == 1 and few32["block_m"] == 32 and few32["block_n"] == 16
+    mid32 = pgg.plan_desc(desc(M=2048, N=4096, G=16, K=7168, batch=256, topk=8, dy=F32))
+    assert mid32["regime"] == 2 and mid32["block_m"] == 128
     decode = pgg.plan_desc(desc(M=128, N=4096, G=16, K=7168, batch=16, topk=8, dy=BF16))
     assert decode["regime"] == 1 and decode["max_chunks"] == 1        # one chunk: pure slot order
     large = pgg.plan_desc(desc(M=110592, N=2048, G=60, K=7168, batch=13824, topk=8, dy=F16))
@@ -100,12 +103,14 @@ def test_plan_regimes():
 
 
 def test_regime_choice_at_measured_shapes():
-    # producer family per rows per expert where both were timed on an MI355X
-    # (uniform routing, topK 8): regime 1 = weight sweep, 2 = fp32 128 x 128
-    # tiles, 0 = 256 x 256 tiles
+    # producer family per rows per expert where the candidates were timed on
+    # an MI355X (uniform routing, topK 8): regime 1 = weight sweep, 2 = fp32
+    # 128 x 128 tiles, 0 = 256 x 256 tiles
     for g, k, n, dt, per, want in ((16, 7168, 4096, BF16, 24, 1), (16, 7168, 4096, BF16, 32, 0),
                                    (60, 7168, 2048, F16, 24, 1), (60, 7168, 2048, F16, 32, 0),
                                    (64, 2048, 1408, BF16, 16, 1), (64, 2048, 1408, BF16, 32, 0),
+                                   (16, 7168, 4096, F32, 8, 1), (16, 7168, 4096, F32, 48, 1),
+                                   (64, 2048, 1408, F32, 32, 1),
                                    (16, 7168, 4096, F32, 128, 2), (16, 7168, 4096, F32, 192, 0),
                                    (16, 7168, 4096, F32, 512, 2), (60, 7168, 2048, F32, 512, 2),
                                    (60, 7168, 2048, F32, 1024, 0)):
