@@ -192,7 +192,7 @@ typedef struct {
   int32_t max_chunks;      /* chunks enqueued per panel */
   int32_t ring_rows;       /* rows of one ring buffer: min(tiles_per_chunk * block_m, M) */
   int32_t fused_prep;      /* 1 when index preparation runs in one workgroup: a kernel of its
-                              own, or -- one-chunk weight-streaming plans with G <= 64, when
+                              own, or -- one-chunk weight-streaming plans with G <= 256, when
                               the rows are 16-byte aligned -- a spare workgroup of the
                               producer launch; 0: three preparation kernels */
   int32_t n_panels;        /* column panels: the output columns are cut into panels of

@@ -191,13 +191,20 @@ __global__ __launch_bounds__(kSwThreads) void sweep_dma_kernel(SweepArgs a) {
     }
     --bid;
     --nwg;
-    // lane g of every wave reads group g (at most 64 groups) and the wave
-    // reduces: total rows, total tiles, any count outside [0, M]
+    // lane l of every wave reads groups l, l + 64, ... and the wave reduces:
+    // total rows, total tiles, any count outside [0, M] (at most
+    // kSweepPrepMaxGroups groups of at most M rows: no overflow)
     const int l = static_cast<int>(threadIdx.x & 63);
-    const int64_t c = l < a.prep.G ? a.gl[l] : 0;
-    const bool bad = __any(c < 0 || c > a.prep.M);
-    int64_t rows = c;
-    int tiles = static_cast<int>((max<int64_t>(c, 0) + 16 * kSwMS - 1) / (16 * kSwMS));
+    int64_t rows = 0;
+    int tiles = 0;
+    bool out_of_range = false;
+    for (int g = l; g < a.prep.G; g += 64) {
+      const int64_t c = a.gl[g];
+      out_of_range |= c < 0 || c > a.prep.M;
+      rows += c;
+      tiles += static_cast<int>((max<int64_t>(c, 0) + 16 * kSwMS - 1) / (16 * kSwMS));
+    }
+    const bool bad = __any(out_of_range);
 #pragma unroll
     for (int d = 32; d >= 1; d >>= 1) {
       rows += __shfl_xor(rows, d);

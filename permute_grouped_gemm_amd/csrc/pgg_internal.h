@@ -135,7 +135,7 @@ hipError_t launch_produce_sweep(const Plan& p, int chunk, const void* grad_y, co
 // One-chunk weight-sweep plans with aligned rows and few groups: the producer
 // launch also runs the index preparation (in a spare workgroup), replacing
 // the preparation kernel.
-constexpr int64_t kSweepPrepMaxGroups = 64;
+constexpr int64_t kSweepPrepMaxGroups = 256;
 bool sweep_can_prepare(const Plan& p, bool aligned);
 hipError_t launch_produce_sweep_prepared(const Plan& p, const void* grad_y, const void* weight,
                                          const int64_t* eri, const int64_t* gl, const WsView& w,

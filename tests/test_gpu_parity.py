@@ -397,10 +397,11 @@ def test_large_f32_all_tokens_and_deterministic(orc, name):
 
 # ---------------------------------------------------------------- preparation placement
 
-@pytest.mark.parametrize("G,empty", [(64, (0, 63)), (80, (5,))])
+@pytest.mark.parametrize("G,empty", [(64, (0, 63)), (80, (5,)), (256, (0, 100, 255)), (300, (7,))])
 def test_stream_group_count_around_producer_preparation(orc, G, empty):
-    # up to 64 groups the sweep producer prepares the indices itself; above,
-    # a preparation kernel runs first -- both must give the oracle's result
+    # up to 256 groups the sweep producer prepares the indices itself (each
+    # lane reading every 64th group); above, a preparation kernel runs first
+    # -- both must give the oracle's result
     case = synth.make_case(40, 8, G, 512, 256, "bf16", seed=700, empty=empty, name=f"G{G}")
     gy, w, eri, gl = upload(case)
     assert pgg.plan(gy, w, eri, gl, case.batch, case.topk, 0)["regime"] == 1
