@@ -101,19 +101,6 @@ struct Operands {
   __amdgpu_buffer_rsrc_t a, b;
 };
 
-// A byte offset past every operand buffer (they are below 2^31 bytes).
-constexpr uint32_t kOutside = 0x80000000u;
-
-// Direct buffer -> LDS load of 16 bytes per lane: lane i's bytes (at byte
-// offset voff of the buffer; zeros when voff is past its range) land at LDS
-// byte offset m0 + 16 i.  Issued by inline assembly like dma16.  An LDS load
-// reads M0 one wait state after it is written, hence the s_nop; the whole
-// offset is in the vector offset, which the range check covers.
-__device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t m0) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :: "s"(m0), "v"(voff), "s"(r) : "memory", "m0");
-}
-
 __device__ __forceinline__ int slot_of(int r, int c) { return c ^ ((r >> 1) & 7); }
 
 template <class T>

@@ -25,7 +25,9 @@
 //
 // Rows that are 16-byte aligned take sweep_dma_kernel: stages of 512 bytes
 // per row; the weight slab (16 rows) and the tile's d_y rows (16 or 32) of a
-// stage are loaded straight into LDS, two rows per wave instruction (512-byte
+// stage are loaded straight into LDS through buffer resources that end at
+// the unit's last weight row and the tile's last d_y row (so rows past them
+// read zeros with no memory access), two rows per wave instruction (512-byte
 // contiguous runs), three stages deep, so a stage's loads are issued two
 // stages before it is multiplied and never drained at a stage boundary; two
 // workgroups per CU overlap one's multiply with the other's waits.  Other
@@ -118,7 +120,9 @@ __device__ __forceinline__ void mma16<TF32>(f32x4_t& acc, u32x4_t a, u32x4_t b) 
 template <class E>
 struct Unit {
   const E* A;         // first d_y row of the m-tile
+  __amdgpu_buffer_rsrc_t a_buf;   // the m-tile's d_y rows, exactly: rows past them read zeros
   const E* B;         // first weight row of the unit
+  __amdgpu_buffer_rsrc_t b_buf;   // the unit's weight rows, exactly
   int rows, cols;     // valid d_y rows (<= 32) and weight rows (<= 16)
   int64_t ring_row;   // ring row of the tile's first row
   int64_t k0;         // first output column
@@ -132,7 +136,13 @@ __device__ __forceinline__ Unit<E> make_unit(const SweepArgs& a, const MTile& ti
   x.k0 = static_cast<int64_t>(kb) * kSwRows;
   x.cols = static_cast<int>(min<int64_t>(kSwRows, a.K - x.k0));
   x.A = static_cast<const E*>(a.A) + static_cast<int64_t>(tile.row0) * a.N;
+  x.a_buf = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<E*>(x.A), 0, static_cast<int>(static_cast<uint32_t>(tile.rows) * uint32_t(a.N * sizeof(E))),
+      0x00020000);
   x.B = static_cast<const E*>(a.B) + (static_cast<int64_t>(tile.g) * a.K + x.k0) * a.N;
+  x.b_buf = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<E*>(x.B), 0, static_cast<int>(static_cast<uint32_t>(x.cols) * uint32_t(a.N * sizeof(E))),
+      0x00020000);
   x.ring_row = static_cast<int64_t>(tile.row0) - chunk_base;
   return x;
 }
@@ -245,7 +255,6 @@ __global__ __launch_bounds__(kSwThreads) void sweep_dma_kernel(SweepArgs a) {
   const int lg = lane >> 4;
   const int sub = lane / kDmaChunks;   // row of a wave instruction this lane loads
   const int ci = lane % kDmaChunks;    // LDS slot it fills
-  const void* zero = &kZero16;
   const uint32_t lds_base = lds_offset(lds);
 
   // step cursor: (tile t, column block kb, stage st)
@@ -311,28 +320,39 @@ __global__ __launch_bounds__(kSwThreads) void sweep_dma_kernel(SweepArgs a) {
   // has rows there, and first, so a wait that assumes the shorter count only
   // ever over-waits on it.
   // weight slabs are read once per call: non-temporal loads; d_y rows are
-  // read by every unit of their tile
-  auto load_block = [&](const E* base, int rows, int row0, uint32_t dst, int64_t nc, bool nt) {
+  // read by every unit of their tile, through the tile's buffer resource, so
+  // rows past the tile cost no memory access
+  const uint32_t row_bytes = static_cast<uint32_t>(N * sizeof(E));
+  auto load_block_w = [&](const Unit<E>& x, uint32_t dst, int64_t nc) {
+#pragma unroll
+    for (int l = 0; l < kDmaLoads; ++l) {
+      const int r0 = (4 * l + wave) * kDmaRPI;
+      const int r = r0 + sub;
+      const int64_t n = (nc + (ci ^ (r & 15))) * EPC;
+      const uint32_t voff = n < N ? static_cast<uint32_t>(r) * row_bytes + static_cast<uint32_t>(n * sizeof(E))
+                                  : kOutside;
+      dma16_buf_nt(x.b_buf, voff, dst + static_cast<uint32_t>(r0 * kDmaChunks) * 16u);
+    }
+  };
+  // r * row_bytes < 2^31 (the host runs this kernel only when 32 rows span
+  // less than 2^31 bytes): no wrap from kOutside
+  auto load_block_a = [&](const Unit<E>& x, int row0, uint32_t dst, int64_t nc) {
 #pragma unroll
     for (int l = 0; l < kDmaLoads; ++l) {
       const int r0 = row0 + (4 * l + wave) * kDmaRPI;
       const int r = r0 + sub;
       const int64_t n = (nc + (ci ^ (r & 15))) * EPC;
-      const bool ok = r < rows && n < N;
-      if (nt)
-        dma16_nt(ok ? static_cast<const void*>(base + static_cast<int64_t>(r) * N + n) : zero,
-                 dst + static_cast<uint32_t>(r0 * kDmaChunks) * 16u);
-      else
-        dma16(ok ? static_cast<const void*>(base + static_cast<int64_t>(r) * N + n) : zero,
-              dst + static_cast<uint32_t>(r0 * kDmaChunks) * 16u);
+      const uint32_t voff = n < N ? static_cast<uint32_t>(r) * row_bytes + static_cast<uint32_t>(n * sizeof(E))
+                                  : kOutside;
+      dma16_buf(x.a_buf, voff, dst + static_cast<uint32_t>(r0 * kDmaChunks) * 16u);
     }
   };
   auto issue = [&](const Cursor& c, int buf) {
     const uint32_t stage = lds_base + static_cast<uint32_t>(buf * kDmaStageSlots) * 16u;
     const int64_t nc = static_cast<int64_t>(c.st) * kDmaChunks;
-    if (c.x.rows > 16) load_block(c.x.A, c.x.rows, 16, stage + kDmaSlotsW * 16u, nc, false);
-    load_block(c.x.B, c.x.cols, 0, stage, nc, true);
-    load_block(c.x.A, c.x.rows, 0, stage + kDmaSlotsW * 16u, nc, false);
+    if (c.x.rows > 16) load_block_a(c.x, 16, stage + kDmaSlotsW * 16u, nc);
+    load_block_w(c.x, stage, nc);
+    load_block_a(c.x, 0, stage + kDmaSlotsW * 16u, nc);
   };
 
   f32x4_t acc[kSwMS];
@@ -508,6 +528,13 @@ __global__ __launch_bounds__(kSwThreads) void sweep_reg_kernel(SweepArgs a) {
   }
 }
 
+// The direct-to-LDS sweep addresses an m-tile's d_y rows through a buffer
+// resource: 32 rows must span less than 2^31 bytes.
+bool sweep_dma_fits(const Plan& p) {
+  const int64_t elem = p.dtype == PGG_F32 ? 4 : 2;
+  return int64_t(16 * kSwMS) * p.N * elem < (int64_t(1) << 31);
+}
+
 template <class T>
 hipError_t launch_typed(const Plan& p, const SweepArgs& args, bool aligned, bool fused, hipStream_t s) {
   const int64_t units = static_cast<int64_t>(p.tc) * p.n_col_tiles;
@@ -516,7 +543,7 @@ hipError_t launch_typed(const Plan& p, const SweepArgs& args, bool aligned, bool
     // is lent to the preparation for its few microseconds)
     const dim3 grid(static_cast<unsigned>(std::min<int64_t>(units, kDmaGrid - 1) + 1));
     hipLaunchKernelGGL((sweep_dma_kernel<T, true>), grid, dim3(kSwThreads), 0, s, args);
-  } else if (aligned) {
+  } else if (aligned && sweep_dma_fits(p)) {
     const dim3 grid(static_cast<unsigned>(std::min<int64_t>(units, kDmaGrid)));
     hipLaunchKernelGGL((sweep_dma_kernel<T, false>), grid, dim3(kSwThreads), 0, s, args);
   } else {
@@ -557,7 +584,7 @@ hipError_t launch(const Plan& p, const SweepArgs& a, bool aligned, bool fused, h
 }  // namespace
 
 bool sweep_can_prepare(const Plan& p, bool aligned) {
-  return aligned && p.regime == kStream && p.n_panels == 1 && p.max_chunks == 1 &&
+  return aligned && sweep_dma_fits(p) && p.regime == kStream && p.n_panels == 1 && p.max_chunks == 1 &&
          p.G <= kSweepPrepMaxGroups;
 }
 

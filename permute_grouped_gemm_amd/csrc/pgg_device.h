@@ -106,17 +106,37 @@ __device__ const u32x4_t kZero16 = {0u, 0u, 0u, 0u};
 // byte offset m0 + 16 i.  Issued by inline assembly, so the compiler neither
 // tracks nor waits for it: the waits on the vector-memory counter are explicit
 // (vector memory operations complete in issue order, and these loads write no
-// register).
+// register).  An LDS load reads M0 one wait state after a scalar write of it
+// (a hazard the compiler cannot see inside the asm), hence the s_nop.
 __device__ __forceinline__ void dma16(const void* src, uint32_t m0) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
                :: "s"(m0), "v"(src) : "memory", "m0");
 }
 
 // The same load with the non-temporal hint: for data read exactly once (a
 // weight stream), so its lines do not displace operands that are reused.
 __device__ __forceinline__ void dma16_nt(const void* src, uint32_t m0) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off nt"
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt"
                :: "s"(m0), "v"(src) : "memory", "m0");
+}
+
+// A byte offset past every buffer the buffer loads below read (each spans
+// less than 2^31 bytes).
+constexpr uint32_t kOutside = 0x80000000u;
+
+// Direct buffer -> LDS load of 16 bytes per lane: lane i's bytes (at byte
+// offset voff of the buffer; zeros, with no memory access, when voff is past
+// its range) land at LDS byte offset m0 + 16 i.  The whole offset is in the
+// vector offset, which the range check covers.
+__device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(m0), "v"(voff), "s"(r) : "memory", "m0");
+}
+
+// The same with the non-temporal hint (a weight stream read once).
+__device__ __forceinline__ void dma16_buf_nt(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
+               :: "s"(m0), "v"(voff), "s"(r) : "memory", "m0");
 }
 
 // Wait until at most N of this wave's vector memory operations are
