@@ -40,7 +40,9 @@
 //
 // Operands are loaded through buffer resources that end at the tile's last
 // row, so rows past the tile's rows or past K read zeros; chunks past N get an
-// offset outside every buffer and read zeros too.  Ring stores
+// offset outside every buffer and read zeros too.  Weight slabs carry the
+// non-temporal hint (NT_B) when the plan expects about one m-tile per expert,
+// so that no other tile reads them again.  Ring stores
 // are ordinary (temporal) stores: the consumer, which reads each ring row once
 // with non-temporal loads right after this launch, then finds part of the
 // ring in the last-level cache.
@@ -103,7 +105,7 @@ struct Operands {
 
 __device__ __forceinline__ int slot_of(int r, int c) { return c ^ ((r >> 1) & 7); }
 
-template <class T>
+template <class T, bool NT_B>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void produce_large_kernel(LargeArgs a) {
   using E = typename T::elem;
@@ -192,9 +194,12 @@ void produce_large_kernel(LargeArgs a) {
       dma16_buf(o.a, (in_n ? voff[j] : kOutside) + koff,
                 base + static_cast<uint32_t>((j * kWaves + wave) * 64 * 16));
 #pragma unroll
-    for (int j = 0; j < kLoadsB; ++j)
-      dma16_buf(o.b, (in_n ? voff[j] : kOutside) + koff,
-                base + static_cast<uint32_t>((kSlotsA + (j * kWaves + wave) * 64) * 16));
+    for (int j = 0; j < kLoadsB; ++j) {
+      const uint32_t vo = (in_n ? voff[j] : kOutside) + koff;
+      const uint32_t m0 = base + static_cast<uint32_t>((kSlotsA + (j * kWaves + wave) * 64) * 16);
+      if constexpr (NT_B) dma16_buf_nt(o.b, vo, m0);
+      else dma16_buf(o.b, vo, m0);
+    }
   };
   // fragment rows start at multiples of 32, so (row >> 1) & 7 == (lr >> 1) & 7
   auto load_frags = [&](int s, int q, u32x4_t (&fa)[kFM], u32x4_t (&fb)[kFN]) {
@@ -366,15 +371,18 @@ hipError_t launch_produce_dma(const Plan& p, int chunk, int panel, const void* g
   int64_t grid = std::min<int64_t>(span, kRound);
   const int64_t need = (span + kMaxTilesPerWg - 1) / kMaxTilesPerWg;
   if (grid < need) grid = (need + kRound - 1) / kRound * kRound;
-  if (p.dtype == PGG_BF16)
-    hipLaunchKernelGGL(produce_large_kernel<TBf16>, dim3(static_cast<unsigned>(grid)), dim3(kThreads),
-                       0, s, a);
-  else if (p.dtype == PGG_F32)
-    hipLaunchKernelGGL(produce_large_kernel<TF32>, dim3(static_cast<unsigned>(grid)), dim3(kThreads),
-                       0, s, a);
-  else
-    hipLaunchKernelGGL(produce_large_kernel<TF16>, dim3(static_cast<unsigned>(grid)), dim3(kThreads),
-                       0, s, a);
+  const dim3 g(static_cast<unsigned>(grid)), b(kThreads);
+  const bool nt = p.stream_weights;
+  if (p.dtype == PGG_BF16) {
+    if (nt) hipLaunchKernelGGL((produce_large_kernel<TBf16, true>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((produce_large_kernel<TBf16, false>), g, b, 0, s, a);
+  } else if (p.dtype == PGG_F32) {
+    if (nt) hipLaunchKernelGGL((produce_large_kernel<TF32, true>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((produce_large_kernel<TF32, false>), g, b, 0, s, a);
+  } else {
+    if (nt) hipLaunchKernelGGL((produce_large_kernel<TF16, true>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((produce_large_kernel<TF16, false>), g, b, 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -63,6 +63,9 @@ struct Plan {
   int32_t ksplit;      // forward, few rows per expert: reduction splits (partials in the ring region)
   int32_t kspan;       // reduction elements per split
   bool fused_prep;
+  // large tiles with about one m-tile per expert: each weight slab is read
+  // once, so its loads carry the non-temporal hint
+  bool stream_weights;
   // layout (byte offsets into the workspace)
   size_t off_header, off_offsets, off_tiles, off_chunks, off_inv, off_ori, off_ring, total;
   size_t ring_bytes, table_bytes;
