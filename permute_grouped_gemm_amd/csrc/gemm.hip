@@ -5,8 +5,9 @@
 // (MoeInitRoutingGroupedMatmulGrad design page, §数学定义和公式 Step 1; the
 // page's cube output type is fp32 whatever the input type, §2.6.2), for the
 // m-tiles of one chunk, written into that chunk's fp32 ring rows.  This file
-// holds the general register-staged tile: 128x128 for fp32 inputs with few
-// rows per expert, 256x256 for rows that are not 16-byte aligned.  Aligned
+// holds the general register-staged tile: 64x128 or 128x128 for fp32 inputs
+// with a middling number of rows per expert, 256x256 for rows that are not
+// 16-byte aligned.  Aligned
 // rows with many rows per expert take the direct-to-LDS 256x256 tile (every
 // input type), and 16-bit inputs with few rows per expert the weight sweep.
 //
@@ -264,8 +265,9 @@ hipError_t launch_produce(const Plan& p, int chunk, int panel, const void* grad_
     case PGG_BF16: return launch_typed<TBf16>(p, args, aligned, s);
     case PGG_F16: return launch_typed<TF16>(p, args, aligned, s);
     default:
-      return p.regime == kLarge ? launch_cfg<TF32, 256, 256, 2, 2>(p, args, aligned, s)
-                                : launch_cfg<TF32, 128, 128, 2, 2>(p, args, aligned, s);
+      if (p.regime == kLarge) return launch_cfg<TF32, 256, 256, 2, 2>(p, args, aligned, s);
+      return p.bm == 64 ? launch_cfg<TF32, 64, 128, 2, 2>(p, args, aligned, s)
+                        : launch_cfg<TF32, 128, 128, 2, 2>(p, args, aligned, s);
   }
 }
 

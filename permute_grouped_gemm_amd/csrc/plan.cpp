@@ -105,31 +105,41 @@ int64_t expected_tiles(const Plan& q, int64_t max_tiles) {
   return std::max<int64_t>(lo, std::min<int64_t>(est, max_tiles));
 }
 
-// Producer family.  Measured on MI355X with uniform routing (K x N of 7168 x
-// 4096, 7168 x 2048 and 2048 x 1408; 16, 60 and 64 experts):
+// Producer family, and for the fp32 tiles their height.  Measured on MI355X
+// with uniform routing (K x N of 7168 x 4096, 7168 x 2048 and 2048 x 1408;
+// 16, 60 and 64 experts):
 //  - 16-bit: the weight sweep reads every expert's weights once per 32-row
 //    m-tile, the 256 x 256 tiles once per 256 rows.  The sweep is faster up
 //    to 24 rows per expert (197 against 236 us, 405 against 456 us) and the
 //    tiles from 32 (240 against 253 us, 473 against 534 us, 112 against 140
 //    us), so the sweep takes M <= 28 G.
-//  - fp32 up to 48 rows per expert: the weight sweep (fp32 MFMAs on the same
-//    staged chunks) against the 128 x 128 tile, which is bound by its MFMAs
-//    on padding rows: 359 against 1057 us at 8 rows per expert, 606 against
-//    1070 at 32, 921 against 1078 at 48 (16 experts, 7168 x 4096).
-//  - fp32 above that: both tiles are bound by the fp32 MFMAs, which also
-//    multiply the padding rows of each expert's last m-tile.  The large tile is taken
-//    when its expected padded rows take less time at relative rates of 0.85
-//    (256 x 256) and 0.78 (128 x 128), fitted to the measured choices: the
-//    large tile at 192 and 1024 rows per expert and at the large fp32 shape
-//    (1.95 against 2.19 ms, 16.05 against 16.51 ms, 25.4 against 27.4 ms),
-//    the small one at 32-128, 256, 384 and 512 (1.64 against 1.92 ms at 128,
-//    4.33 against 4.84 ms at 512).
-bool few_rows_per_expert(const Plan& q) {
-  if (q.dtype != PGG_F32) return q.M <= 28 * q.G;
-  if (q.M <= 48 * q.G) return true;   // the fp32 weight sweep
-  const double t256 = expected_tiles_per_expert(q, 256) * 256.0 / 0.85;
-  const double t128 = expected_tiles_per_expert(q, 128) * 128.0 / 0.78;
-  return t128 <= t256;
+//  - fp32 up to 32 rows per expert: the weight sweep (fp32 MFMAs on the same
+//    staged chunks), 359 against 1057 us for the 128 x 128 tile at 8 rows
+//    per expert (16 experts, 7168 x 4096); at 32 it ties with the 64 x 128
+//    tile (606 against about 600 us) and at 48 it loses (921 against 598).
+//  - fp32 above that: the tiles are bound by the fp32 MFMAs, which also
+//    multiply the padding rows of each expert's last m-tile.  The tile with
+//    the least expected padded rows at its relative rate is taken: 0.73 for
+//    64 x 128, 0.78 for 128 x 128 and 0.85 for the direct-to-LDS 256 x 256,
+//    fitted to the measured choices: 64 rows at 48-64, 128-256 rows per
+//    expert (598 against 1081 us at 48, 1469 against 1631 at 128), 128 rows
+//    at 96 (1100 against 1175 us), 256 rows at 192 and 1024 and at the large
+//    fp32 shape (1.95 against 2.04 ms, 16.05 against 16.51 ms, 25.4 against
+//    27.4 ms).
+struct Family {
+  int32_t regime;
+  int32_t bm;   // fp32 tile rows (kF32 only)
+};
+
+Family choose_family(const Plan& q) {
+  if (q.dtype != PGG_F32) return {q.M <= 28 * q.G ? kStream : kLarge, 0};
+  const double c64 = expected_tiles_per_expert(q, 64) * 64.0 / 0.73;
+  const double c128 = expected_tiles_per_expert(q, 128) * 128.0 / 0.78;
+  const double c256 = expected_tiles_per_expert(q, 256) * 256.0 / 0.85;
+  const int32_t bm = c64 <= c128 ? 64 : 128;
+  if (q.M <= 32 * q.G) return {kStream, bm};
+  if (c256 < std::min(c64, c128)) return {kLarge, bm};
+  return {kF32, bm};
 }
 
 int choose_panels(const Plan& q, size_t budget, int64_t max_tiles) {
@@ -179,8 +189,8 @@ int choose_panels(const Plan& q, size_t budget, int64_t max_tiles) {
 
 // Output tile per regime: large-M MFMA tiles (every input type); for few rows
 // per expert, m-tiles of 32 rows crossed with units of 16 weight rows that a
-// persistent grid streams in address order; for fp32 in between, 128 x 128
-// tiles.
+// persistent grid streams in address order; for fp32 in between, tiles 128
+// wide and 64 or 128 rows high (the height chosen with the family).
 TileShape tile_shape(int32_t regime) {
   switch (regime) {
     case kLarge: return {256, 256};
@@ -223,10 +233,9 @@ pgg_status plan_with_budget(const pgg_moe_dx_desc* d, size_t budget, Plan* p) {
   q.panel_cols = q.K;
   q.dtype = d->grad_y_dtype;
   // few rows per expert: the weight sweep, or for fp32 between the sweep and
-  // the large tile the 128 x 128 tile
-  if (!few_rows_per_expert(q)) q.regime = kLarge;
-  else if (q.dtype == PGG_F32 && q.M > 48 * q.G) q.regime = kF32;
-  else q.regime = kStream;
+  // the large tile the 64 x 128 or 128 x 128 tile
+  const Family fam = choose_family(q);
+  q.regime = fam.regime;
   // Non-temporal weight loads in the large tiles pay when each expert has
   // about one 256-row m-tile, so no other tile reads its slabs (measured:
   // 6-9 % faster at 64-128 rows per expert, 4-7 % slower at the large and mid
@@ -239,7 +248,7 @@ pgg_status plan_with_budget(const pgg_moe_dx_desc* d, size_t budget, Plan* p) {
     else if (!strcmp(e, "sweep")) q.regime = kStream;
   }
   const TileShape ts = tile_shape(q.regime);
-  q.bm = ts.bm;
+  q.bm = q.regime == kF32 ? fam.bm : ts.bm;
   q.bn = ts.bn;
   const int64_t max_tiles = (M + q.bm - 1) / q.bm + G;
   if (max_tiles >= (int64_t(1) << 31)) return PGG_ERR_UNSUPPORTED;

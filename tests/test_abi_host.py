@@ -93,7 +93,7 @@ def test_plan_regimes():
     few32 = pgg.plan_desc(desc(M=128, N=4096, G=16, K=7168, batch=16, topk=8, dy=F32))
     assert few32["regime"] == 1 and few32["block_m"] == 32 and few32["block_n"] == 16
     mid32 = pgg.plan_desc(desc(M=2048, N=4096, G=16, K=7168, batch=256, topk=8, dy=F32))
-    assert mid32["regime"] == 2 and mid32["block_m"] == 128
+    assert mid32["regime"] == 2 and mid32["block_m"] == 64 and mid32["block_n"] == 128
     decode = pgg.plan_desc(desc(M=128, N=4096, G=16, K=7168, batch=16, topk=8, dy=BF16))
     assert decode["regime"] == 1 and decode["max_chunks"] == 1        # one chunk: pure slot order
     large = pgg.plan_desc(desc(M=110592, N=2048, G=60, K=7168, batch=13824, topk=8, dy=F16))
@@ -103,20 +103,22 @@ def test_plan_regimes():
 
 
 def test_regime_choice_at_measured_shapes():
-    # producer family per rows per expert where the candidates were timed on
-    # an MI355X (uniform routing, topK 8): regime 1 = weight sweep, 2 = fp32
-    # 128 x 128 tiles, 0 = 256 x 256 tiles
-    for g, k, n, dt, per, want in ((16, 7168, 4096, BF16, 24, 1), (16, 7168, 4096, BF16, 32, 0),
-                                   (60, 7168, 2048, F16, 24, 1), (60, 7168, 2048, F16, 32, 0),
-                                   (64, 2048, 1408, BF16, 16, 1), (64, 2048, 1408, BF16, 32, 0),
-                                   (16, 7168, 4096, F32, 8, 1), (16, 7168, 4096, F32, 48, 1),
-                                   (64, 2048, 1408, F32, 32, 1),
-                                   (16, 7168, 4096, F32, 128, 2), (16, 7168, 4096, F32, 192, 0),
-                                   (16, 7168, 4096, F32, 512, 2), (60, 7168, 2048, F32, 512, 2),
-                                   (60, 7168, 2048, F32, 1024, 0)):
+    # producer family (and fp32 tile height) per rows per expert where the
+    # candidates were timed on an MI355X (uniform routing, topK 8): regime 1 =
+    # weight sweep, 2 = fp32 register-staged tiles, 0 = 256 x 256 tiles
+    for g, k, n, dt, per, want, bm in (
+            (16, 7168, 4096, BF16, 24, 1, 32), (16, 7168, 4096, BF16, 32, 0, 256),
+            (60, 7168, 2048, F16, 24, 1, 32), (60, 7168, 2048, F16, 32, 0, 256),
+            (64, 2048, 1408, BF16, 16, 1, 32), (64, 2048, 1408, BF16, 32, 0, 256),
+            (16, 7168, 4096, F32, 8, 1, 32), (16, 7168, 4096, F32, 32, 1, 32),
+            (64, 2048, 1408, F32, 32, 1, 32),
+            (16, 7168, 4096, F32, 48, 2, 64), (60, 7168, 2048, F32, 64, 2, 64),
+            (16, 7168, 4096, F32, 96, 2, 128), (16, 7168, 4096, F32, 128, 2, 64),
+            (16, 7168, 4096, F32, 192, 0, 256), (60, 7168, 2048, F32, 256, 2, 64),
+            (60, 7168, 2048, F32, 512, 2, 128), (60, 7168, 2048, F32, 1024, 0, 256)):
         m = g * per
         p = pgg.plan_desc(desc(M=m, N=n, G=g, K=k, batch=m // 8, topk=8, dy=dt))
-        assert p["regime"] == want, (g, k, n, dt, per, p)
+        assert (p["regime"], p["block_m"]) == (want, bm), (g, k, n, dt, per, p)
 
 
 def test_panel_choice_at_measured_shapes():
