@@ -385,3 +385,36 @@ def test_unpermute_descriptor_checks():
     assert L.pgg_moe_unpermute(ctypes.byref(d), None, fake, fake, fake, fake, n.value, None) == pgg.ERR_INVALID_ARG
     # with probabilities the gradient needs permuted and probs_grad
     assert L.pgg_moe_unpermute_grad(ctypes.byref(d), None, fake, fake, fake, fake, fake, fake, n.value, None) == pgg.ERR_INVALID_ARG
+
+
+# ---------------------------------------------------------------- plan invariants over random shapes
+
+from hypothesis import given, settings, strategies as st
+
+
+@settings(max_examples=400, deadline=None)
+@given(batch=st.integers(1, 40000), topk=st.integers(1, 8), G=st.integers(1, 300),
+       K=st.integers(1, 9000), N=st.integers(1, 9000), dt=st.sampled_from([F32, F16, BF16]))
+def test_plan_invariants_on_random_shapes(batch, topk, G, K, N, dt):
+    # whatever the family, tile height and panels the estimates pick, the
+    # plan's tables, chunks and ring stay consistent and bounded
+    M = batch * topk
+    d = desc(M=M, N=N, G=G, K=K, batch=batch, topk=topk, dy=dt)
+    st_, size = status_of_size(d)
+    assert st_ == pgg.OK
+    p = pgg.plan_desc(d)
+    shape = (p["regime"], p["block_m"], p["block_n"])
+    assert shape in {(0, 256, 256), (1, 32, 16), (2, 64, 128), (2, 128, 128)}, shape
+    assert p["regime"] != 2 or dt == F32
+    assert p["max_tiles"] == -(-M // p["block_m"]) + G
+    assert p["max_chunks"] * p["tiles_per_chunk"] >= p["max_tiles"] >= 1
+    assert p["ring_rows"] == min(p["tiles_per_chunk"] * p["block_m"], M)
+    w = p["panel_cols"]
+    assert p["n_panels"] == -(-K // w) and 0 < w <= K
+    assert w == K or w % p["block_n"] == 0
+    if p["regime"] == 1:
+        assert p["n_panels"] == 1
+    assert p["ring_bytes"] == p["ring_rows"] * w * 4 <= min(M * K * 4, 256 << 20)
+    # regions are 512-byte aligned
+    assert p["workspace_bytes"] == p["table_bytes"] + -(-p["ring_bytes"] // 512) * 512 == size
+    assert p["table_bytes"] % 512 == 0
