@@ -245,6 +245,24 @@ def _stream_handle(stream) -> int:
     return int(s.cuda_stream)
 
 
+def _check_inputs(*tensors):
+    dev = tensors[0].device
+    for t in tensors:
+        if not t.is_cuda or not t.is_contiguous() or t.device != dev:
+            raise PggError(ERR_INVALID_ARG, "inputs must be contiguous tensors on one GPU")
+
+
+def _check_workspace(workspace, dev):
+    if workspace.device != dev or not workspace.is_contiguous():
+        raise PggError(ERR_INVALID_ARG, "workspace must be a contiguous tensor on the inputs' GPU")
+
+
+def _check_out(out, batch, weight, dev):
+    if (out.dtype != torch.float32 or not out.is_contiguous() or out.device != dev
+            or tuple(out.shape) != (int(batch), int(weight.shape[1]))):
+        raise PggError(ERR_INVALID_ARG, "out must be a contiguous float32 [batch, K] tensor on the inputs' GPU")
+
+
 def moe_dx(grad_y: torch.Tensor, weight: torch.Tensor, expanded_row_idx: torch.Tensor,
            group_list: torch.Tensor, batch: int, topk: int, row_idx_type: int = 0, *,
            out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
@@ -256,17 +274,15 @@ def moe_dx(grad_y: torch.Tensor, weight: torch.Tensor, expanded_row_idx: torch.T
     GPU.  ``workspace`` (uint8, at least ``workspace_size(...)`` bytes,
     256-byte aligned) and ``out`` may be passed to avoid allocations."""
     d = _desc_from_tensors(grad_y, weight, expanded_row_idx, group_list, batch, topk, row_idx_type)
-    for t in (grad_y, weight, expanded_row_idx, group_list):
-        if not t.is_cuda or not t.is_contiguous():
-            raise PggError(ERR_INVALID_ARG, "inputs must be contiguous GPU tensors")
+    _check_inputs(grad_y, weight, expanded_row_idx, group_list)
     need = workspace_size_desc(d)
     dev = grad_y.device
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     if out is None:
         out = torch.empty((int(batch), int(weight.shape[1])), dtype=torch.float32, device=dev)
-    if out.dtype != torch.float32 or not out.is_contiguous() or tuple(out.shape) != (int(batch), int(weight.shape[1])):
-        raise PggError(ERR_INVALID_ARG, "out must be a contiguous float32 [batch, K] tensor")
+    _check_out(out, batch, weight, dev)
+    _check_workspace(workspace, dev)
     st = lib().pgg_moe_dx(ctypes.byref(d), grad_y.data_ptr(), weight.data_ptr(),
                           expanded_row_idx.data_ptr(), group_list.data_ptr(), out.data_ptr(),
                           workspace.data_ptr(), workspace.numel() * workspace.element_size(),
@@ -283,14 +299,11 @@ def moe_dx_noalloc(grad_y: torch.Tensor, weight: torch.Tensor, expanded_row_idx:
     with the library's fixed device scratch as workspace; ``device_error``
     (optional int64 [2] on the GPU) receives [code, detail] of this call."""
     d = _desc_from_tensors(grad_y, weight, expanded_row_idx, group_list, batch, topk, row_idx_type)
-    for t in (grad_y, weight, expanded_row_idx, group_list):
-        if not t.is_cuda or not t.is_contiguous():
-            raise PggError(ERR_INVALID_ARG, "inputs must be contiguous GPU tensors")
-    if out.dtype != torch.float32 or not out.is_contiguous() or tuple(out.shape) != (int(batch), int(weight.shape[1])):
-        raise PggError(ERR_INVALID_ARG, "out must be a contiguous float32 [batch, K] tensor")
+    _check_inputs(grad_y, weight, expanded_row_idx, group_list)
+    _check_out(out, batch, weight, grad_y.device)
     if device_error is not None and (device_error.dtype != torch.int64 or device_error.numel() < 2
-                                     or not device_error.is_cuda):
-        raise PggError(ERR_INVALID_ARG, "device_error must be a GPU int64 tensor of 2 elements")
+                                     or device_error.device != grad_y.device):
+        raise PggError(ERR_INVALID_ARG, "device_error must be an int64 tensor of 2 elements on the inputs' GPU")
     st = lib().pgg_moe_dx_noalloc(ctypes.byref(d), grad_y.data_ptr(), weight.data_ptr(),
                                   expanded_row_idx.data_ptr(), group_list.data_ptr(), out.data_ptr(),
                                   None if device_error is None else device_error.data_ptr(),
@@ -411,8 +424,10 @@ def _fwd_buffers(d, x, weight, out, workspace):
     shape = (int(d.batch * d.topk), int(weight.shape[2]))
     if out is None:
         out = torch.empty(shape, dtype=torch.float32, device=dev)
-    if out.dtype != torch.float32 or not out.is_contiguous() or tuple(out.shape) != shape:
-        raise PggError(ERR_INVALID_ARG, "out must be a contiguous float32 [M, N] tensor")
+    if (out.dtype != torch.float32 or not out.is_contiguous() or tuple(out.shape) != shape
+            or out.device != dev):
+        raise PggError(ERR_INVALID_ARG, "out must be a contiguous float32 [M, N] tensor on the inputs' GPU")
+    _check_workspace(workspace, dev)
     return out, workspace
 
 
@@ -425,9 +440,7 @@ def moe_fwd(x: torch.Tensor, weight: torch.Tensor, expanded_row_idx: torch.Tenso
     x [batch, K] and weight [G, K, N] share one of float32 / float16 /
     bfloat16; expanded_row_idx [batch*topk] and group_list [G] are int64."""
     d = _fwd_desc_from_tensors(x, weight, expanded_row_idx, group_list, topk, row_idx_type)
-    for t in (x, weight, expanded_row_idx, group_list):
-        if not t.is_cuda or not t.is_contiguous():
-            raise PggError(ERR_INVALID_ARG, "inputs must be contiguous GPU tensors")
+    _check_inputs(x, weight, expanded_row_idx, group_list)
     out, workspace = _fwd_buffers(d, x, weight, out, workspace)
     st = lib().pgg_moe_fwd(ctypes.byref(d), x.data_ptr(), weight.data_ptr(),
                            expanded_row_idx.data_ptr(), group_list.data_ptr(), out.data_ptr(),
@@ -483,8 +496,10 @@ def _dw_buffers(d, x, out, workspace):
     shape = (int(d.weight_groups), int(d.weight_rows), int(d.weight_cols))
     if out is None:
         out = torch.empty(shape, dtype=torch.float32, device=dev)
-    if out.dtype != torch.float32 or not out.is_contiguous() or tuple(out.shape) != shape:
-        raise PggError(ERR_INVALID_ARG, "out must be a contiguous float32 [G, K, N] tensor")
+    if (out.dtype != torch.float32 or not out.is_contiguous() or tuple(out.shape) != shape
+            or out.device != dev):
+        raise PggError(ERR_INVALID_ARG, "out must be a contiguous float32 [G, K, N] tensor on the inputs' GPU")
+    _check_workspace(workspace, dev)
     return out, workspace
 
 
@@ -496,9 +511,7 @@ def moe_dw(x: torch.Tensor, grad_y: torch.Tensor, expanded_row_idx: torch.Tensor
     g's expanded rows)^T · grad_y[those rows] (asynchronous).  x [batch, K] and
     grad_y [batch*topk, N] share one of float32 / float16 / bfloat16."""
     d = _dw_desc_from_tensors(x, grad_y, expanded_row_idx, group_list, topk, row_idx_type)
-    for t in (x, grad_y, expanded_row_idx, group_list):
-        if not t.is_cuda or not t.is_contiguous():
-            raise PggError(ERR_INVALID_ARG, "inputs must be contiguous GPU tensors")
+    _check_inputs(x, grad_y, expanded_row_idx, group_list)
     out, workspace = _dw_buffers(d, x, out, workspace)
     st = lib().pgg_moe_dw(ctypes.byref(d), x.data_ptr(), grad_y.data_ptr(),
                           expanded_row_idx.data_ptr(), group_list.data_ptr(), out.data_ptr(),
@@ -554,13 +567,14 @@ def moe_routing(expert_ids: torch.Tensor, experts: int, x: Optional[torch.Tensor
     batch, topk = expert_ids.shape
     K, xd = 0, 0
     if x is not None:
-        if x.dim() != 2 or x.shape[0] != batch or not x.is_cuda or not x.is_contiguous():
-            raise PggError(ERR_INVALID_ARG, "x must be a contiguous GPU [batch, K] tensor")
+        if x.dim() != 2 or x.shape[0] != batch or x.device != expert_ids.device or not x.is_contiguous():
+            raise PggError(ERR_INVALID_ARG, "x must be a contiguous [batch, K] tensor on expert_ids' GPU")
         K, xd = x.shape[1], DTYPE_CODE.get(x.dtype, -1)
     d = make_routing_desc(batch, topk, experts, K, xd)
     dev = expert_ids.device
     if workspace is None:
         workspace = torch.empty(routing_workspace_size_desc(d), dtype=torch.uint8, device=dev)
+    _check_workspace(workspace, dev)
     M = batch * topk
     gl = torch.empty(int(experts), dtype=torch.int64, device=dev)
     eg = torch.empty(M, dtype=torch.int64, device=dev) if gather else None
@@ -583,8 +597,25 @@ def make_unpermute_desc(batch, topk, hidden, row_idx_type, dtype) -> UnpermuteDe
     return d
 
 
+def _check_value(t, shape, like, name):
+    """t: a contiguous 2-D tensor of like's dtype on like's GPU (of `shape` when given)."""
+    if (t.dim() != 2 or not t.is_contiguous() or t.device != like.device or not t.is_cuda
+            or t.dtype != like.dtype or (shape is not None and tuple(t.shape) != shape)):
+        want = "" if shape is None else f" {list(shape)}"
+        raise PggError(ERR_INVALID_ARG, f"{name} must be a contiguous{want} {like.dtype} GPU tensor "
+                                        f"on {like.device}")
+
+
+def _check_index(t, n, like):
+    if t.dtype != torch.int64 or t.dim() != 1 or t.numel() != n or not t.is_contiguous() \
+            or t.device != like.device:
+        raise PggError(ERR_INVALID_ARG, f"expanded_row_idx must be a contiguous int64 [{n}] tensor "
+                                        f"on {like.device}")
+
+
 def _unpermute_ws(d, dev, workspace):
     if workspace is not None:
+        _check_workspace(workspace, dev)
         return workspace
     n = ctypes.c_size_t()
     _check(lib().pgg_moe_unpermute_workspace_size(ctypes.byref(d), ctypes.byref(n)),
@@ -598,7 +629,13 @@ def moe_unpermute(permuted: torch.Tensor, expanded_row_idx: torch.Tensor, batch:
     """MoeTokenUnpermute: with probs [batch, topk], out [batch, H] = sum over
     slots of probs * the token's expert rows; without, the gather [M, H].
     permuted [batch*topk, H]; results in permuted's dtype (fp32 arithmetic)."""
+    M = int(batch) * int(topk)
+    _check_value(permuted, None, permuted, "permuted")
     H = permuted.shape[1]
+    _check_value(permuted, (M, H), permuted, "permuted")
+    _check_index(expanded_row_idx, M, permuted)
+    if probs is not None:
+        _check_value(probs, (int(batch), int(topk)), permuted, "probs")
     d = make_unpermute_desc(batch, topk, H, row_idx_type, DTYPE_CODE.get(permuted.dtype, -1))
     shape = (int(batch), H) if probs is not None else (int(batch) * int(topk), H)
     out = torch.empty(shape, dtype=permuted.dtype, device=permuted.device)
@@ -616,9 +653,17 @@ def moe_unpermute_grad(grad: torch.Tensor, expanded_row_idx: torch.Tensor, batch
     """MoeTokenUnpermuteGrad: (perm_grad [M, H], probs_grad [batch, topk] or
     None).  With probs, grad is [batch, H] and permuted is needed; without,
     grad is [M, H] and perm_grad its scatter back to expanded rows."""
-    H = grad.shape[1]
-    d = make_unpermute_desc(batch, topk, H, row_idx_type, DTYPE_CODE.get(grad.dtype, -1))
     M = int(batch) * int(topk)
+    _check_value(grad, None, grad, "grad")
+    H = grad.shape[1]
+    _check_value(grad, (int(batch) if probs is not None else M, H), grad, "grad")
+    _check_index(expanded_row_idx, M, grad)
+    if probs is not None:
+        _check_value(probs, (int(batch), int(topk)), grad, "probs")
+        if permuted is None:
+            raise PggError(ERR_INVALID_ARG, "permuted is needed with probs")
+        _check_value(permuted, (M, H), grad, "permuted")
+    d = make_unpermute_desc(batch, topk, H, row_idx_type, DTYPE_CODE.get(grad.dtype, -1))
     perm_grad = torch.empty((M, H), dtype=grad.dtype, device=grad.device)
     probs_grad = (torch.empty((int(batch), int(topk)), dtype=grad.dtype, device=grad.device)
                   if probs is not None else None)

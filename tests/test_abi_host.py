@@ -418,3 +418,21 @@ def test_plan_invariants_on_random_shapes(batch, topk, G, K, N, dt):
     # regions are 512-byte aligned
     assert p["workspace_bytes"] == p["table_bytes"] + -(-p["ring_bytes"] // 512) * 512 == size
     assert p["table_bytes"] % 512 == 0
+
+
+def test_binding_rejects_host_tensors_before_any_call():
+    # every entry point checks that its tensors are contiguous GPU tensors of
+    # the described shapes before it hands a pointer to the library
+    import torch
+    y = torch.zeros((8, 16), dtype=torch.bfloat16)
+    w = torch.zeros((2, 24, 16), dtype=torch.bfloat16)
+    eri = torch.arange(8, dtype=torch.int64)
+    gl = torch.tensor([4, 4], dtype=torch.int64)
+    with pytest.raises(pgg.PggError):
+        pgg.moe_dx(y, w, eri, gl, 4, 2)
+    with pytest.raises(pgg.PggError):
+        pgg.moe_unpermute(y, eri, 4, 2)
+    with pytest.raises(pgg.PggError):
+        pgg.moe_unpermute_grad(y, eri, 4, 2)
+    with pytest.raises(pgg.PggError):
+        pgg.moe_routing(torch.zeros((4, 2), dtype=torch.int64), 2)
