@@ -64,7 +64,7 @@ int64_t tiles_per_chunk(int bm, int64_t cols, size_t budget, int64_t max_tiles) 
 //    true m-tile count is known only on the device; rounds are counted at
 //    its expectation under routing that is uniform over the experts
 //    (expected_tiles), cut into chunks of the plan's size (which the bound
-//    sets).  The bound (M / 256 plus one partial tile per every expert)
+//    sets).  The bound (M / 256 plus one partial tile per expert)
 //    overstates a launch by up to G / 2 m-tiles, which at 64 experts of
 //    about 512 rows (K 7168, N 2048) made 7 panels of one chunk look as fast
 //    as 2 panels of three, against 1.52 and 1.38 ms measured.
@@ -85,13 +85,16 @@ int64_t producer_rounds(const Plan& q, int64_t w, int64_t tc, int64_t tiles) {
 // Expected m-tiles of bm rows per expert when each token's topK experts are
 // distinct and uniform: an expert's row count is then Binomial(batch, topK /
 // G), and E[ceil(c / bm)] = sum_j P(c > j bm), taken from the normal
-// approximation with continuity correction.
+// approximation with continuity correction.  Terms more than 8 standard
+// deviations below the mean are 1 and are counted without the loop, so the
+// loop runs over at most 16 sd / bm + 2 terms.
 double expected_tiles_per_expert(const Plan& q, int bm) {
   const double p = std::min(1.0, double(q.topk) / double(q.G));
   const double mu = double(q.batch) * p;
   const double sd = std::sqrt(double(q.batch) * p * (1.0 - p));
-  double per_expert = 0.0;
-  for (int64_t j = 0; double(j) * bm < mu + 8.0 * sd + 1.0; ++j) {
+  const int64_t j0 = static_cast<int64_t>(std::max(0.0, mu - 8.0 * sd - 1.0) / bm);
+  double per_expert = double(j0);
+  for (int64_t j = j0; double(j) * bm < mu + 8.0 * sd + 1.0; ++j) {
     const double x = double(j) * bm;
     per_expert += sd > 0.0 ? 0.5 * std::erfc((x + 0.5 - mu) / (sd * std::sqrt(2.0))) : (mu > x ? 1.0 : 0.0);
   }

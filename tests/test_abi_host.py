@@ -436,3 +436,14 @@ def test_binding_rejects_host_tensors_before_any_call():
         pgg.moe_unpermute_grad(y, eri, 4, 2)
     with pytest.raises(pgg.PggError):
         pgg.moe_routing(torch.zeros((4, 2), dtype=torch.int64), 2)
+
+
+def test_plan_time_does_not_grow_with_M():
+    # the planner's expected-tile estimate sums only the terms near the mean
+    # row count, so planning a 2^30-row call costs what a small one does
+    import time
+    t = time.perf_counter()
+    for m, g, topk in ((1 << 30, 1, 1), ((1 << 30) - 2, 2, 2), (1 << 29, 64, 8)):
+        pgg.plan_desc(desc(M=m, N=64, G=g, K=64, batch=m // topk, topk=topk, dy=BF16))
+        pgg.plan_desc(desc(M=m, N=64, G=g, K=64, batch=m // topk, topk=topk, dy=F32))
+    assert time.perf_counter() - t < 0.25
