@@ -31,8 +31,11 @@ CASES = [
     # large tiles, many chunks of one panel: row consumer
     ("large_tiles_rows", {"PGG_RING_MB": "1", "PGG_PANEL_COLS": "100000"},
      dict(batch=300, topk=4, G=6, K=1024, N=256, dtype="bf16")),
-    # fp32 tiles
+    # fp32 tiles (64 rows high here)
     ("f32_tiles", {}, dict(batch=200, topk=4, G=5, K=600, N=264, dtype="f32")),
+    # fp32 weight sweep with the index preparation inside its launch
+    ("f32_sweep_prepared", {}, dict(batch=16, topk=8, G=16, K=2048, N=1024, dtype="f32",
+                                    empty=(2, 7))),
     # rows not 16-byte aligned: register-staged tiles
     ("unaligned_rows", {}, dict(batch=100, topk=3, G=4, K=700, N=286, dtype="bf16")),
 ]

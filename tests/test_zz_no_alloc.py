@@ -53,10 +53,11 @@ def test_noalloc_matches_moe_dx_on_two_calls_second_smaller():
     np.testing.assert_array_equal(bits(got), bits(want))
 
 
-def test_noalloc_weight_streaming_and_repeat():
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_noalloc_weight_streaming_and_repeat(dtype):
     # decode-sized call (the weight sweep prepares the indices in its own
     # launch): equal to pgg_moe_dx bit for bit, and on a repeat
-    case = synth.make_case(16, 8, 16, 2048, 1024, "bf16", seed=902, empty=(1, 5, 9))
+    case = synth.make_case(16, 8, 16, 2048, 1024, dtype, seed=902, empty=(1, 5, 9))
     t = upload(case)
     want = run(case, tensors=t)
     for _ in range(2):
