@@ -222,7 +222,9 @@ hipError_t launch_cfg(const Plan& p, const GemmArgs& args, bool aligned, hipStre
 template <class T>
 hipError_t launch_typed(const Plan& p, const GemmArgs& args, bool aligned, hipStream_t s) {
   switch (p.regime) {
-    case kLarge: return launch_cfg<T, 256, 256, 2, 2>(p, args, aligned, s);
+    case kLarge:   // rows that are not 16-byte aligned, or too short a reduction
+      return p.bm == 128 ? launch_cfg<T, 128, 256, 2, 2>(p, args, aligned, s)
+                         : launch_cfg<T, 256, 256, 2, 2>(p, args, aligned, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -54,34 +54,47 @@ namespace pgg {
 
 namespace {
 
-constexpr int kBM = 256, kBN = 256;
+constexpr int kBN = 256;
 constexpr int kThreads = 512, kWaves = 8;    // two waves per SIMD
 constexpr int kWM = 2;                        // waves along rows
-constexpr int kWTM = 128, kWTN = 64;          // wave tile
-constexpr int kFM = kWTM / 32, kFN = kWTN / 32;
+constexpr int kWTN = 64;                      // wave tile columns
+constexpr int kFN = kWTN / 32;
 constexpr int kRowChunks = 8;                 // 16-byte chunks per LDS row per stage
 // reduction elements per stage: 128 bytes of each row
 template <class T>
 constexpr int stage_elems() { return kRowChunks * T::kPerChunk; }
 constexpr int kPairs = kRowChunks / 2;
-constexpr int kStages = 2;
-constexpr int kSlotsA = kBM * kRowChunks;
 constexpr int kSlotsB = kBN * kRowChunks;
-constexpr int kStageSlots = kSlotsA + kSlotsB;
 constexpr int kRowsPerLoad = 64 / kRowChunks;          // rows one wave instruction covers
 constexpr int kLoadRows = kRowsPerLoad * kWaves;       // rows one load index covers across the waves
-constexpr int kLoadsA = kSlotsA / kThreads;            // direct-to-LDS loads per thread per stage
-constexpr int kLoadsB = kSlotsB / kThreads;
-constexpr int kLoadsPerStage = kLoadsA + kLoadsB;
+constexpr int kLoadsB = kSlotsB / kThreads;            // direct-to-LDS loads per thread per stage
 constexpr int kSuperM = 8, kSuperN = 4;                // super-block of tiles per XCD round
 constexpr int kSuper = kSuperM * kSuperN;
 constexpr int kXcds = 8;
 constexpr int kRound = kXcds * kSuper;                 // tiles of one raster round (256)
 constexpr int kMaxTilesPerWg = 64;                     // LDS tile-table entries per workgroup
-static_assert(kLoadsPerStage * kStages <= 63, "vmcnt range");
 static_assert(kPairs % 2 == 0, "a stage must end on the second fragment set");
-static_assert(kRowsPerLoad * kWaves * kLoadsA == kBM && kRowsPerLoad * kWaves * kLoadsB == kBN,
-              "loads cover the tile rows");
+static_assert(kRowsPerLoad * kWaves * kLoadsB == kBN, "loads cover the tile columns");
+
+// Tile heights.  256 rows with two LDS stages for many rows per expert; 128
+// rows with three stages (two in flight at each barrier) when each expert has
+// about one 128-row m-tile, where the weight stream, not the multiply, is the
+// bound and the extra stage in flight streams it faster.
+template <int BM>
+struct Shape {
+  static constexpr int kStages = BM == 256 ? 2 : 3;
+  static constexpr int kWTM = BM / kWM;                // wave tile rows
+  static constexpr int kFM = kWTM / 32;
+  static constexpr int kSlotsA = BM * kRowChunks;
+  static constexpr int kStageSlots = kSlotsA + kSlotsB;
+  static constexpr int kLoadsA = kSlotsA / kThreads;
+  static constexpr int kLoadsPerStage = kLoadsA + kLoadsB;
+  static constexpr int kLoadsMax = kLoadsA > kLoadsB ? kLoadsA : kLoadsB;
+  static_assert(BM == 256 || BM == 128, "tile heights");
+  static_assert(kLoadsPerStage * kStages <= 63, "vmcnt range");
+  static_assert(kRowsPerLoad * kWaves * kLoadsA == BM, "loads cover the tile rows");
+  static_assert(kFM * kFN >= kFM + kFN, "a pair's MFMAs read every fragment of the next pair");
+};
 
 struct LargeArgs {
   const void* A;            // grad_y [M, N]
@@ -105,10 +118,14 @@ struct Operands {
 
 __device__ __forceinline__ int slot_of(int r, int c) { return c ^ ((r >> 1) & 7); }
 
-template <class T, bool NT_B>
+template <class T, bool NT_B, int BM>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void produce_large_kernel(LargeArgs a) {
   using E = typename T::elem;
+  using Sh = Shape<BM>;
+  constexpr int kStages = Sh::kStages, kWTM = Sh::kWTM, kFM = Sh::kFM;
+  constexpr int kSlotsA = Sh::kSlotsA, kStageSlots = Sh::kStageSlots;
+  constexpr int kLoadsA = Sh::kLoadsA, kLoadsPerStage = Sh::kLoadsPerStage, kLoadsMax = Sh::kLoadsMax;
   constexpr int kBK = stage_elems<T>();
   __shared__ u32x4_t lds[kStages * kStageSlots];
   // this workgroup's tiles: {g, row0, rows, column tile}; rows 0 = no tile
@@ -165,9 +182,9 @@ void produce_large_kernel(LargeArgs a) {
   const uint32_t row_bytes = static_cast<uint32_t>(N * sizeof(E));
   // byte offset of load j's row chunk within a tile's operand buffer (the
   // same for d_y and weight rows)
-  uint32_t voff[kLoadsA];
+  uint32_t voff[kLoadsMax];
 #pragma unroll
-  for (int j = 0; j < kLoadsA; ++j)
+  for (int j = 0; j < kLoadsMax; ++j)
     voff[j] = static_cast<uint32_t>(r0 + kLoadRows * j) * row_bytes + static_cast<uint32_t>(dma_c * 16);
 
   auto operands = [&](int j) {
@@ -246,18 +263,29 @@ void produce_large_kernel(LargeArgs a) {
   Operands on = nxt < n_mine ? operands(nxt) : oc;
   // stage d of the stream counted from the current tile's first stage: the
   // current tile's, or -- past its last -- the next tile's, into LDS slot
-  // (d + par) & 1.  d <= nk + 1 < 2 nk, since the host runs this kernel only
-  // for nk >= 2, so the stream never reaches past the next tile.
+  // (d + par) mod kStages.  d <= nk + kStages - 1 < 2 nk, since the host runs
+  // this kernel only for nk >= kStages, so the stream never reaches past the
+  // next tile.  With three stages, each barrier waits for all but the last
+  // stage's loads, so past the stream's end a stage of zeros (every offset
+  // past its buffer: no memory access) keeps that count; it lands in a slot
+  // nobody reads again.
   auto issue_stream = [&](int d, int par) {
-    if (d < nk) issue(oc, d, (d + par) & 1);
-    else if (nxt < n_mine) issue(on, d - nk, (d + par) & 1);
+    if constexpr (kStages == 2) {
+      if (d < nk) issue(oc, d, (d + par) & 1);
+      else if (nxt < n_mine) issue(on, d - nk, (d + par) & 1);
+    } else {
+      if (d < nk) issue(oc, d, (d + par) % kStages);
+      else if (nxt < n_mine) issue(on, d - nk, (d + par) % kStages);
+      else issue(oc, nk, (d + par) % kStages);
+    }
   };
   int par = 0;   // LDS slot of the current tile's stage 0
   issue_stream(0, par);
-  issue_stream(1, par);   // nk > 1 (the host's choice of this kernel), so stage 1 exists
+  issue_stream(1, par);
+  if constexpr (kStages > 2) issue_stream(2, par);
   u32x4_t fa0[kFM], fb0[kFN], fa1[kFM], fb1[kFN];
-  // stage 0 landed (stage 1 may still be in flight)
-  wait_then_barrier<kLoadsPerStage>();
+  // stage 0 landed (the later ones may still be in flight)
+  wait_then_barrier<(kStages - 1) * kLoadsPerStage>();
   load_frags(par, 0, fa0, fb0);
   for (;;) {
 #pragma unroll
@@ -268,26 +296,26 @@ void produce_large_kernel(LargeArgs a) {
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
     const bool more = nxt < n_mine;
     for (int kt = 0; kt < nk; ++kt) {
-      const int s = (kt + par) & 1;
+      const int s = kStages == 2 ? (kt + par) & 1 : (kt + par) % kStages;
 #pragma unroll
       for (int q = 0; q + 1 < kPairs; ++q) {
         if (q & 1) mfmas_reading(fa1, fb1, s, q + 1, fa0, fb0);
         else mfmas_reading(fa0, fb0, s, q + 1, fa1, fb1);
       }
       // Last pair: the stream's next stage landed everywhere and every wave
-      // is done with this one; its slot is refilled with the stage two ahead
-      // by the first wave of each SIMD before its last MFMAs of the stage and
+      // is done with this one; its slot is refilled with the stage kStages
+      // ahead by the first wave of each SIMD before its last MFMAs of the stage and
       // by the second after them, so one of the two is always feeding the
       // matrix unit.  This runs unconditionally: issue_stream skips stages
       // past the stream's end, and after the last stage the barrier and the
       // fragment reads are merely idle.  A branch here would join ahead of
       // these MFMAs with the next stage's reads in flight, and the compiler
       // then waits for those reads before the MFMAs.
-      wait_then_barrier<0>();
-      if (wave < kWaves / 2) issue_stream(kt + 2, par);
-      load_frags(s ^ 1, 0, fa0, fb0);
+      wait_then_barrier<(kStages - 2) * kLoadsPerStage>();
+      if (wave < kWaves / 2) issue_stream(kt + kStages, par);
+      load_frags(kStages == 2 ? s ^ 1 : (kt + 1 + par) % kStages, 0, fa0, fb0);
       mfmas(fa1, fb1);
-      if (wave >= kWaves / 2) issue_stream(kt + 2, par);
+      if (wave >= kWaves / 2) issue_stream(kt + kStages, par);
     }
 
     // Epilogue: accumulator v of lane (lr, lh) is row 8*(v/4) + 4*lh + v%4,
@@ -325,13 +353,16 @@ void produce_large_kernel(LargeArgs a) {
       }
     }
     if (!more) break;
-    // the next tile becomes current; its first stage sits in slot par ^ (nk & 1)
-    par = (par + nk) & 1;
+    // the next tile becomes current; its first stage sits in slot (par + nk) mod kStages
+    par = kStages == 2 ? (par + nk) & 1 : (par + nk) % kStages;
     cur = nxt;
     oc = on;
     nxt = next_tile(cur + 1);
     if (nxt < n_mine) on = operands(nxt);
   }
+  // the stages of zeros issued past the stream's end land before the
+  // workgroup's LDS is released
+  if constexpr (kStages > 2) wait_then_barrier<0>();
 }
 
 }  // namespace
@@ -342,7 +373,9 @@ void produce_large_kernel(LargeArgs a) {
 // register-staged tile.
 bool produce_uses_dma(const Plan& p, bool aligned) {
   const int64_t bk = p.dtype == PGG_F32 ? stage_elems<TF32>() : stage_elems<TBf16>();
-  return aligned && p.regime == kLarge && p.N > bk &&
+  // at least kStages stages of the reduction
+  const bool shape = p.bm == 256 ? p.N > bk : p.bm == 128 && p.dtype != PGG_F32 && p.N > 2 * bk;
+  return aligned && p.regime == kLarge && shape &&
          p.N < (int64_t(1) << 22) && p.panel_cols < (int64_t(1) << 21);
 }
 
@@ -373,15 +406,18 @@ hipError_t launch_produce_dma(const Plan& p, int chunk, int panel, const void* g
   if (grid < need) grid = (need + kRound - 1) / kRound * kRound;
   const dim3 g(static_cast<unsigned>(grid)), b(kThreads);
   const bool nt = p.stream_weights;
-  if (p.dtype == PGG_BF16) {
-    if (nt) hipLaunchKernelGGL((produce_large_kernel<TBf16, true>), g, b, 0, s, a);
-    else hipLaunchKernelGGL((produce_large_kernel<TBf16, false>), g, b, 0, s, a);
+  if (p.bm == 128) {   // 16-bit, about one m-tile per expert: weight stream, non-temporal
+    if (p.dtype == PGG_BF16) hipLaunchKernelGGL((produce_large_kernel<TBf16, true, 128>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((produce_large_kernel<TF16, true, 128>), g, b, 0, s, a);
+  } else if (p.dtype == PGG_BF16) {
+    if (nt) hipLaunchKernelGGL((produce_large_kernel<TBf16, true, 256>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((produce_large_kernel<TBf16, false, 256>), g, b, 0, s, a);
   } else if (p.dtype == PGG_F32) {
-    if (nt) hipLaunchKernelGGL((produce_large_kernel<TF32, true>), g, b, 0, s, a);
-    else hipLaunchKernelGGL((produce_large_kernel<TF32, false>), g, b, 0, s, a);
+    if (nt) hipLaunchKernelGGL((produce_large_kernel<TF32, true, 256>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((produce_large_kernel<TF32, false, 256>), g, b, 0, s, a);
   } else {
-    if (nt) hipLaunchKernelGGL((produce_large_kernel<TF16, true>), g, b, 0, s, a);
-    else hipLaunchKernelGGL((produce_large_kernel<TF16, false>), g, b, 0, s, a);
+    if (nt) hipLaunchKernelGGL((produce_large_kernel<TF16, true, 256>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((produce_large_kernel<TF16, false, 256>), g, b, 0, s, a);
   }
   return hipGetLastError();
 }

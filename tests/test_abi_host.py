@@ -103,13 +103,15 @@ def test_plan_regimes():
 
 
 def test_regime_choice_at_measured_shapes():
-    # producer family (and fp32 tile height) per rows per expert where the
+    # producer family and tile height per rows per expert where the
     # candidates were timed on an MI355X (uniform routing, topK 8): regime 1 =
-    # weight sweep, 2 = fp32 register-staged tiles, 0 = 256 x 256 tiles
+    # weight sweep, 2 = fp32 register-staged tiles, 0 = 256- or 128-row tiles
     for g, k, n, dt, per, want, bm in (
-            (16, 7168, 4096, BF16, 24, 1, 32), (16, 7168, 4096, BF16, 32, 0, 256),
-            (60, 7168, 2048, F16, 24, 1, 32), (60, 7168, 2048, F16, 32, 0, 256),
-            (64, 2048, 1408, BF16, 16, 1, 32), (64, 2048, 1408, BF16, 32, 0, 256),
+            (16, 7168, 4096, BF16, 24, 1, 32), (16, 7168, 4096, BF16, 32, 0, 128),
+            (60, 7168, 2048, F16, 24, 1, 32), (60, 7168, 2048, F16, 32, 0, 128),
+            (64, 2048, 1408, BF16, 16, 1, 32), (64, 2048, 1408, BF16, 32, 0, 128),
+            (16, 7168, 4096, BF16, 96, 0, 128), (16, 7168, 4096, BF16, 128, 0, 256),
+            (60, 7168, 2048, F16, 128, 0, 256),
             (16, 7168, 4096, F32, 8, 1, 32), (16, 7168, 4096, F32, 32, 1, 32),
             (64, 2048, 1408, F32, 32, 1, 32),
             (16, 7168, 4096, F32, 48, 2, 64), (60, 7168, 2048, F32, 64, 2, 64),
@@ -404,7 +406,8 @@ def test_plan_invariants_on_random_shapes(batch, topk, G, K, N, dt):
     assert st_ == pgg.OK
     p = pgg.plan_desc(d)
     shape = (p["regime"], p["block_m"], p["block_n"])
-    assert shape in {(0, 256, 256), (1, 32, 16), (2, 64, 128), (2, 128, 128)}, shape
+    assert shape in {(0, 256, 256), (0, 128, 256), (1, 32, 16), (2, 64, 128), (2, 128, 128)}, shape
+    assert p["block_m"] != 128 or p["regime"] != 0 or dt != F32
     assert p["regime"] != 2 or dt == F32
     assert p["max_tiles"] == -(-M // p["block_m"]) + G
     assert p["max_chunks"] * p["tiles_per_chunk"] >= p["max_tiles"] >= 1
