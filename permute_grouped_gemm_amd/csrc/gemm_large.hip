@@ -1,8 +1,9 @@
 // Producer for many rows per expert (fp16 / bf16 / fp32, 16-byte aligned
 // rows): the grouped-matmul gradient C[i, k] = sum_n d_y[i, n] * W[g(i), k, n]
 // with fp32 accumulation (MoeInitRoutingGroupedMatmulGrad design page,
-// §数学定义和公式 Step 1; fp32 cube output, §2.6.2) on 256x256 output tiles,
-// written into the chunk's ring rows.  fp32 inputs run the same tile: a
+// §数学定义和公式 Step 1; fp32 cube output, §2.6.2) on output tiles of 256
+// columns and 256 rows (or 128 rows, for 16-bit inputs with about one such
+// m-tile per expert), written into the chunk's ring rows.  fp32 inputs run the same tile: a
 // 16-byte chunk then holds 4 reduction elements instead of 8, so a stage
 // covers 32 of them, and each fragment pair feeds four 32x32x2 fp32 MFMAs
 // (sixteen times the MFMA time per stage against the same loads).
@@ -18,8 +19,10 @@
 // drain while it multiplies.
 //
 // Operand staging is direct buffer -> LDS (buffer_load_dwordx4 ... lds: lane
-// i's 16 bytes land at M0 + 16 i), two stages of 128 bytes per row (64 KiB
-// each: 256 d_y rows + 256 weight rows of 128 bytes, whole cache lines).  The
+// i's 16 bytes land at M0 + 16 i), stages of 128 bytes per row (whole cache
+// lines): two of 64 KiB (256 d_y rows + 256 weight rows) for the 256-row
+// tile, three of 48 KiB for the 128-row one, whose barriers then leave the
+// stage after next in flight.  The
 // loads are issued by inline assembly so the compiler does not serialise them
 // with a blanket wait before every LDS read; the waits on their counter are
 // explicit (vector memory operations complete in issue order, and these loads
