@@ -157,8 +157,9 @@ pgg_status pgg_moe_dx_noalloc(const pgg_moe_dx_desc* desc, const void* grad_y, c
 /*
  * Read the device error word of the last pgg_moe_dx (or pgg_moe_fwd,
  * pgg_moe_dw, pgg_moe_routing, pgg_moe_unpermute[_grad]) that used `workspace`.
- * Synchronises `stream`.  *code receives a pgg_device_error; *detail its
- * detail value (may be NULL).  When several violations exist, the one with
+ * Synchronises `stream`.  Reads the workspace's first 64 bytes (the error
+ * word's region), which every workspace of those calls holds.  *code
+ * receives a pgg_device_error; *detail its detail value (may be NULL).  When several violations exist, the one with
  * the smallest (code, detail) is reported, so the report is deterministic.
  */
 pgg_status pgg_moe_dx_read_device_error(const void* workspace, hipStream_t stream,
@@ -166,16 +167,18 @@ pgg_status pgg_moe_dx_read_device_error(const void* workspace, hipStream_t strea
 
 /*
  * Copy the index tables the last call built into host arrays (tests only;
- * synchronises `stream`).  inv_host[p] (length M) = expanded row of original
- * position p; ori_host[i] (length M) = original position of expanded row i.
- * Either pointer may be NULL.
+ * synchronises `stream`).  `workspace` is that call's, of the size queried
+ * for `desc`: the tables sit in its first table_bytes (pgg_moe_dx_plan).
+ * inv_host[p] (length M) = expanded row of original position p; ori_host[i]
+ * (length M) = original position of expanded row i.  Either pointer may be
+ * NULL.
  */
 pgg_status pgg_moe_dx_debug_tables(const pgg_moe_dx_desc* desc, const void* workspace,
                                    hipStream_t stream, int32_t* inv_host, int32_t* ori_host);
 
 /*
- * The m-tile table the last call built (tests only; synchronises `stream`):
- * tiles_host receives up to max_tiles entries of 3 int32 (expert, first
+ * The m-tile table the last call built (tests only; synchronises `stream`;
+ * `workspace` as for pgg_moe_dx_debug_tables): tiles_host receives up to max_tiles entries of 3 int32 (expert, first
  * expanded row, row count), in expert order, empty experts contributing none;
  * *n_tiles the number of tiles.
  */

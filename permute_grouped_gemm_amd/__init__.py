@@ -312,7 +312,27 @@ def moe_dx_noalloc(grad_y: torch.Tensor, weight: torch.Tensor, expanded_row_idx:
     return out
 
 
+def _ws_bytes(workspace):
+    return workspace.numel() * workspace.element_size()
+
+
+def _check_tables_workspace(workspace, d, dev):
+    """The debug readers copy index tables out of ``workspace``: it must be the
+    inputs' GPU's workspace of a call with this descriptor (all its tables)."""
+    if not workspace.is_cuda:
+        raise PggError(ERR_INVALID_ARG, "workspace must be a GPU tensor")
+    _check_workspace(workspace, dev)
+    if _ws_bytes(workspace) < plan_desc(d)["table_bytes"]:
+        raise PggError(ERR_WORKSPACE_TOO_SMALL, "workspace smaller than this call's index tables")
+
+
+# the device error word sits in the workspace's first 64 bytes
+_WS_HEADER_BYTES = 64
+
+
 def read_device_error(workspace: torch.Tensor, stream=None) -> Tuple[int, int]:
+    if not workspace.is_cuda or not workspace.is_contiguous() or _ws_bytes(workspace) < _WS_HEADER_BYTES:
+        raise PggError(ERR_INVALID_ARG, "workspace must be a contiguous GPU tensor of a call's workspace")
     code = ctypes.c_int32()
     detail = ctypes.c_int64()
     _check(lib().pgg_moe_dx_read_device_error(workspace.data_ptr(), _stream_handle(stream),
@@ -325,6 +345,7 @@ def debug_tables(grad_y, weight, expanded_row_idx, group_list, batch, topk, row_
                  workspace, stream=None):
     """(inv, ori) int32 host tensors built by the last call on ``workspace``."""
     d = _desc_from_tensors(grad_y, weight, expanded_row_idx, group_list, batch, topk, row_idx_type)
+    _check_tables_workspace(workspace, d, grad_y.device)
     M = d.grad_y_rows
     inv = torch.empty(M, dtype=torch.int32)
     ori = torch.empty(M, dtype=torch.int32)
@@ -338,6 +359,7 @@ def debug_tiles(grad_y, weight, expanded_row_idx, group_list, batch, topk, row_i
                 workspace, stream=None):
     """m-tile table [(expert, first row, rows)] built by the last call on ``workspace``."""
     d = _desc_from_tensors(grad_y, weight, expanded_row_idx, group_list, batch, topk, row_idx_type)
+    _check_tables_workspace(workspace, d, grad_y.device)
     cap = plan_desc(d)["max_tiles"]
     buf = torch.empty(3 * cap, dtype=torch.int32)
     n = ctypes.c_int32()
@@ -642,7 +664,7 @@ def moe_unpermute(permuted: torch.Tensor, expanded_row_idx: torch.Tensor, batch:
     ws = _unpermute_ws(d, permuted.device, workspace)
     st = lib().pgg_moe_unpermute(ctypes.byref(d), permuted.data_ptr(), expanded_row_idx.data_ptr(),
                                  None if probs is None else probs.data_ptr(), out.data_ptr(),
-                                 ws.data_ptr(), ws.numel(), _stream_handle(stream))
+                                 ws.data_ptr(), _ws_bytes(ws), _stream_handle(stream))
     _check(st, "pgg_moe_unpermute")
     return out
 
@@ -671,7 +693,7 @@ def moe_unpermute_grad(grad: torch.Tensor, expanded_row_idx: torch.Tensor, batch
     ptr = lambda t: None if t is None else t.data_ptr()
     st = lib().pgg_moe_unpermute_grad(ctypes.byref(d), ptr(permuted), grad.data_ptr(),
                                       expanded_row_idx.data_ptr(), ptr(probs), perm_grad.data_ptr(),
-                                      ptr(probs_grad), ws.data_ptr(), ws.numel(), _stream_handle(stream))
+                                      ptr(probs_grad), ws.data_ptr(), _ws_bytes(ws), _stream_handle(stream))
     _check(st, "pgg_moe_unpermute_grad")
     return perm_grad, probs_grad
 

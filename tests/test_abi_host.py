@@ -441,6 +441,27 @@ def test_binding_rejects_host_tensors_before_any_call():
         pgg.moe_routing(torch.zeros((4, 2), dtype=torch.int64), 2)
 
 
+def test_binding_checks_the_workspace_of_the_readers():
+    # the readers copy out of a workspace whose size the C ABI is not given,
+    # so the binding rejects host tensors and ones too small for what they read
+    import torch
+    y = torch.zeros((8, 16), dtype=torch.bfloat16)
+    w = torch.zeros((2, 24, 16), dtype=torch.bfloat16)
+    eri = torch.arange(8, dtype=torch.int64)
+    gl = torch.tensor([4, 4], dtype=torch.int64)
+    size = pgg.workspace_size(y, w, eri, gl, 4, 2)
+    for bad in (torch.zeros(size, dtype=torch.uint8), torch.zeros(16, dtype=torch.uint8)):
+        with pytest.raises(pgg.PggError) as e:
+            pgg.read_device_error(bad)
+        assert e.value.status == pgg.ERR_INVALID_ARG
+        with pytest.raises(pgg.PggError) as e:
+            pgg.debug_tables(y, w, eri, gl, 4, 2, 0, bad)
+        assert e.value.status == pgg.ERR_INVALID_ARG
+        with pytest.raises(pgg.PggError) as e:
+            pgg.debug_tiles(y, w, eri, gl, 4, 2, 0, bad)
+        assert e.value.status == pgg.ERR_INVALID_ARG
+
+
 def test_plan_time_does_not_grow_with_M():
     # the planner's expected-tile estimate sums only the terms near the mean
     # row count, so planning a 2^30-row call costs what a small one does

@@ -41,3 +41,24 @@ def test_unpermute_arguments_checked_against_the_descriptor():
     out = pgg.moe_unpermute(perm, eri, batch, topk, 0, probs)
     torch.cuda.synchronize()
     assert out.shape == (batch, H)
+
+
+def test_readers_refuse_a_workspace_smaller_than_what_they_read():
+    case = synth.make_case(16, 2, 4, 64, 32, "bf16", seed=2)
+    gy, w, eri, gl = upload(case)
+    ws = torch.empty(pgg.workspace_size(gy, w, eri, gl, case.batch, case.topk), dtype=torch.uint8,
+                     device=gy.device)
+    pgg.moe_dx(gy, w, eri, gl, case.batch, case.topk, workspace=ws)
+    torch.cuda.synchronize()
+    assert pgg.read_device_error(ws) == (pgg.DEV_OK, 0)
+    with pytest.raises(pgg.PggError) as e:
+        pgg.read_device_error(ws[:32])
+    assert e.value.status == pgg.ERR_INVALID_ARG
+    with pytest.raises(pgg.PggError) as e:
+        pgg.debug_tables(gy, w, eri, gl, case.batch, case.topk, 0, ws[:1024])
+    assert e.value.status == pgg.ERR_WORKSPACE_TOO_SMALL
+    with pytest.raises(pgg.PggError) as e:
+        pgg.debug_tiles(gy, w, eri, gl, case.batch, case.topk, 0, ws[:1024])
+    assert e.value.status == pgg.ERR_WORKSPACE_TOO_SMALL
+    inv, ori = pgg.debug_tables(gy, w, eri, gl, case.batch, case.topk, 0, ws)
+    assert sorted(inv.tolist()) == list(range(case.M)) and sorted(ori.tolist()) == list(range(case.M))
