@@ -375,11 +375,14 @@ def kernel_time(grad_y, weight, expanded_row_idx, group_list, batch, topk, row_i
     (``which="produce"``) or the consumer (``"consume"``), launched back to
     back between two HIP events after one full call (pgg_moe_dx_kernel_time)."""
     d = _desc_from_tensors(grad_y, weight, expanded_row_idx, group_list, batch, topk, row_idx_type)
+    _check_inputs(grad_y, weight, expanded_row_idx, group_list)
     dev = grad_y.device
     if workspace is None:
         workspace = torch.empty(workspace_size_desc(d), dtype=torch.uint8, device=dev)
+    _check_workspace(workspace, dev)
     if out is None:
         out = torch.empty((int(batch), int(weight.shape[1])), dtype=torch.float32, device=dev)
+    _check_out(out, batch, weight, dev)
     avg = ctypes.c_double()
     n = ctypes.c_int32()
     w = {"produce": 0, "consume": 1}[which]

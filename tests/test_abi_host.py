@@ -439,6 +439,8 @@ def test_binding_rejects_host_tensors_before_any_call():
         pgg.moe_unpermute_grad(y, eri, 4, 2)
     with pytest.raises(pgg.PggError):
         pgg.moe_routing(torch.zeros((4, 2), dtype=torch.int64), 2)
+    with pytest.raises(pgg.PggError):
+        pgg.kernel_time(y, w, eri, gl, 4, 2, repeats=1)
 
 
 def test_binding_checks_the_workspace_of_the_readers():
