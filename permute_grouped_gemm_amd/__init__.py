@@ -480,6 +480,7 @@ def fwd_kernel_time(x, weight, expanded_row_idx, group_list, topk, row_idx_type=
     """Average ms of one launch of the forward's grouped-matmul kernel, launched
     back to back after one full call (pgg_moe_fwd_kernel_time)."""
     d = _fwd_desc_from_tensors(x, weight, expanded_row_idx, group_list, topk, row_idx_type)
+    _check_inputs(x, weight, expanded_row_idx, group_list)
     out, workspace = _fwd_buffers(d, x, weight, out, workspace)
     avg = ctypes.c_double()
     _check(lib().pgg_moe_fwd_kernel_time(ctypes.byref(d), x.data_ptr(), weight.data_ptr(),
@@ -551,6 +552,7 @@ def dw_kernel_time(x, grad_y, expanded_row_idx, group_list, topk, row_idx_type=0
     """Average ms of one launch of the weight-gradient kernel, back to back
     after one full call (pgg_moe_dw_kernel_time)."""
     d = _dw_desc_from_tensors(x, grad_y, expanded_row_idx, group_list, topk, row_idx_type)
+    _check_inputs(x, grad_y, expanded_row_idx, group_list)
     out, workspace = _dw_buffers(d, x, out, workspace)
     avg = ctypes.c_double()
     _check(lib().pgg_moe_dw_kernel_time(ctypes.byref(d), x.data_ptr(), grad_y.data_ptr(),

@@ -441,6 +441,14 @@ def test_binding_rejects_host_tensors_before_any_call():
         pgg.moe_routing(torch.zeros((4, 2), dtype=torch.int64), 2)
     with pytest.raises(pgg.PggError):
         pgg.kernel_time(y, w, eri, gl, 4, 2, repeats=1)
+    x = torch.zeros((4, 24), dtype=torch.bfloat16)
+    fw = torch.zeros((2, 24, 16), dtype=torch.bfloat16)
+    for f in (pgg.moe_fwd, pgg.fwd_kernel_time):
+        with pytest.raises(pgg.PggError):
+            f(x, fw, eri, gl, 2)
+    for f in (pgg.moe_dw, pgg.dw_kernel_time):
+        with pytest.raises(pgg.PggError):
+            f(x, y, eri, gl, 2)
 
 
 def test_binding_checks_the_workspace_of_the_readers():
