@@ -5,7 +5,8 @@ The plan picks the producer from the rows per expert (weight sweep, fp32
 16-byte aligned), so shapes drawn around those boundaries, with reduction
 and column tails, exercise every kernel and its edges.  Integer-valued
 inputs make every partial sum exact, so d_x must equal the oracle's
-slot-ordered sum bit for bit.
+slot-ordered sum bit for bit.  The forward and the weight gradient are drawn
+the same way, with aligned variants for their direct-to-LDS tiles.
 """
 import numpy as np
 import pytest
@@ -46,3 +47,44 @@ def test_random_shape_bit_exact(orc, kw):
     print(f"[random] {kw} regime {plan['regime']} block {plan['block_m']}x{plan['block_n']}", flush=True)
     got = run(case, tensors=tensors)
     np.testing.assert_array_equal(bits(got), bits(orc.case_dx(case, mode=orc.SLOT)))
+
+
+# The forward and the weight gradient on shapes drawn the same way: their
+# plans take the 32-row sweep up to 64 rows per expert, the 256 x 256 tiles
+# above (direct-to-LDS when rows are 16-byte aligned) and 128 x 128 tiles for
+# fp32.  Integer-valued x and weights keep every sum exact (|terms| <= 4, at
+# most 700 of them for the forward and 300 * 8 rows per expert for d_weight).
+def _aligned(cases):
+    # K and N rounded up to multiples of 8: 16-byte rows, the direct-to-LDS paths
+    return [dict(c, K=-(-c["K"] // 8) * 8, N=-(-c["N"] // 8) * 8) for c in cases]
+
+
+FWD_CASES = _draw(18, seed=20261204) + _aligned(_draw(9, seed=20261206))
+DW_CASES = _draw(18, seed=20261205) + _aligned(_draw(9, seed=20261207))
+
+
+def _ids(cases):
+    return [f"{c['dtype']}-b{c['batch']}k{c['topk']}G{c['G']}K{c['K']}N{c['N']}" for c in cases]
+
+
+@pytest.mark.parametrize("kw", FWD_CASES, ids=_ids(FWD_CASES))
+def test_random_shape_forward_bit_exact(orc, kw):
+    from test_gpu_fwd import run_fwd, upload_fwd
+    case = synth.make_case(seed=8, integer=True, **kw)
+    x = synth.forward_input(case, integer=True)
+    t = upload_fwd(case, x)
+    print(f"[random fwd] {kw} plan {pgg.fwd_plan(*t, case.topk, case.row_idx_type)}", flush=True)
+    got = run_fwd(case, x, tensors=t)
+    np.testing.assert_array_equal(bits(got), bits(orc.case_fwd(case, x).astype(np.float32)))
+
+
+@pytest.mark.parametrize("kw", DW_CASES, ids=_ids(DW_CASES))
+def test_random_shape_dweight_bit_exact(orc, kw):
+    from test_gpu_dw import run_dw, upload_dw
+    case = synth.make_case(seed=9, integer=True, **kw)
+    x = synth.forward_input(case, integer=True)
+    t = upload_dw(case, x)
+    print(f"[random dw] {kw} M {case.M}", flush=True)
+    got = run_dw(case, x, tensors=t)
+    assert 4 * int(np.max(case.group_list)) < 2 ** 24
+    np.testing.assert_array_equal(bits(got), bits(orc.case_dw(case, x).astype(np.float32)))
