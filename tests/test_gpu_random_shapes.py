@@ -49,6 +49,21 @@ def test_random_shape_bit_exact(orc, kw):
     np.testing.assert_array_equal(bits(got), bits(orc.case_dx(case, mode=orc.SLOT)))
 
 
+# every other drawn shape: all three types (the draw cycles them) and families
+@pytest.mark.parametrize("kw", CASES[::2], ids=[f"{c['dtype']}-b{c['batch']}k{c['topk']}G{c['G']}K{c['K']}N{c['N']}"
+                                               for c in CASES[::2]])
+def test_random_shape_float_parity(orc, kw):
+    # random values (weights N(0, 0.02)) against the oracle's exact sum, under
+    # the normwise and elementwise tolerance rules
+    from parity import check_close
+    case = synth.make_case(seed=11, w_std=0.02, **kw)
+    tensors = upload(case)
+    print(f"[random float] {kw}", flush=True)
+    got = run(case, tensors=tensors)
+    exact, absdot = orc.case_dx(case, mode=orc.EXACT, want_abs=True)
+    check_close(got, exact, absdot, case.N, case.topk, case.dtype, f"random {kw}")
+
+
 # The forward and the weight gradient on shapes drawn the same way: their
 # plans take the 32-row sweep up to 64 rows per expert, the 256 x 256 tiles
 # above (direct-to-LDS when rows are 16-byte aligned) and 128 x 128 tiles for
