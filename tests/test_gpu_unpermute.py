@@ -54,6 +54,16 @@ SHAPES = [(100, 4, 300), (16, 8, 7168), (7, 1, 5), (513, 2, 1031), (5, 20, 264),
           (3, 2, 8200)]
 
 
+def _draw_shapes(n, seed=20261208):
+    # seeded (batch, topK, H) with H on both sides of the register kernel's limit
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return [(int(rng.integers(1, 400)), int(rng.integers(1, 9)), int(rng.integers(1, 5000)))
+            for _ in range(n)]
+
+
+SHAPES += _draw_shapes(6)
+
+
 @pytest.mark.parametrize("shape", SHAPES)
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("rit", [0, 1])
