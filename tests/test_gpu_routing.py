@@ -39,6 +39,21 @@ CASES = [
 ]
 
 
+def _draw(n, seed=20261209):
+    # seeded batch, topK and expert counts from one expert to a few thousand
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = []
+    for i in range(n):
+        G = int(rng.choice([int(rng.integers(1, 64)), int(rng.integers(64, 4000))]))
+        topk = int(rng.integers(1, min(G, 8) + 1))
+        out.append(dict(batch=int(rng.integers(1, 6000)), topk=topk, G=G, seed=100 + i,
+                        routing=("uniform", "zipf")[i % 2]))
+    return out
+
+
+CASES += _draw(8)
+
+
 @pytest.mark.parametrize("kw", CASES)
 def test_routing_tables_bit_exact(orc, kw):
     c = synth.make_case(K=1, N=1, **kw)
