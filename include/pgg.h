@@ -103,10 +103,13 @@ typedef struct {
  * pgg_moe_dx would reject (PGG_ERR_UNSUPPORTED: M >= 2^31, G >= 2^30,
  * N >= 2^31 or K >= 2^29).  The size is O(M + G) integer index tables plus
  * an fp32 tile ring of min(M*K*4 bytes, 256 MiB).
- * Two environment variables, read when a plan is made, tune the schedule
+ * Three environment variables, read when a plan is made, tune the schedule
  * (the size and every call planned under the same setting follow them; a
  * fixed setting gives fixed results): PGG_RING_MB sets the ring bound in MiB
- * (at most 1024), PGG_PANEL_COLS the width of the column panels.
+ * (at most 1024), PGG_PANEL_COLS the width of the column panels (ignored by
+ * the weight sweep, which keeps one panel), and PGG_REGIME the producer
+ * family: "large" (the 256- or 128-row tiles), "few" (the weight sweep, or
+ * for fp32 the 64- or 128-row tiles) or "sweep" (the weight sweep).
  */
 pgg_status pgg_moe_dx_workspace_size(const pgg_moe_dx_desc* desc, size_t* bytes);
 
