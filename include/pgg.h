@@ -8,7 +8,7 @@
  *
  * i.e. the grouped-matmul gradient d_y · Wᵀ (Step 1) fused with the routing
  * scatter-add back to the tokens (Step 2).  fp32 tiles go through a
- * workspace ring of at most 256 MiB, whatever M, and a consumer stage adds
+ * workspace ring of at most 1 GiB, whatever M, and a consumer stage adds
  * them into d_x in a fixed order with no floating-point atomics, so repeated
  * calls give bit-identical results.  The ring holds min(M*K*4 bytes, the
  * bound): when the whole fp32 [M,K] intermediate fits under the bound (small
@@ -102,7 +102,7 @@ typedef struct {
  * call).  Returns PGG_ERR_INVALID_ARG / PGG_ERR_UNSUPPORTED for descriptors
  * pgg_moe_dx would reject (PGG_ERR_UNSUPPORTED: M >= 2^31, G >= 2^30,
  * N >= 2^31 or K >= 2^29).  The size is O(M + G) integer index tables plus
- * an fp32 tile ring of min(M*K*4 bytes, 256 MiB).
+ * an fp32 tile ring of min(M*K*4 bytes, 1 GiB).
  * Three environment variables, read when a plan is made, tune the schedule
  * (the size and every call planned under the same setting follow them; a
  * fixed setting gives fixed results): PGG_RING_MB sets the ring bound in MiB
